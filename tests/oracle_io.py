@@ -1,0 +1,57 @@
+"""Turn a generated workload (storage form) into the oracle's fp64 inputs."""
+
+import numpy as np
+
+import oracle
+
+
+def oracle_inputs(wl, latent_override=None):
+    s = wl.spec
+    lat = latent_override
+    if lat is None:
+        lat = oracle.decode_stored(wl.kv_latent, s.latent_dtype, wl.kv_scale)
+    return {
+        "q_nope": oracle.decode_stored(wl.q_nope, s.act_dtype),
+        "q_rope": oracle.decode_stored(wl.q_rope, s.act_dtype),
+        "w_uk": oracle.decode_stored(wl.w_uk, s.act_dtype),
+        "w_uv": oracle.decode_stored(wl.w_uv, s.act_dtype),
+        "kv_latent": lat,
+        "kv_rope": oracle.decode_stored(wl.kv_rope, s.act_dtype),
+        "block_table": np.asarray(wl.block_table),
+        "seqlens": np.asarray(wl.seqlens),
+        "page_size": s.page_size,
+        "softmax_scale": s.scale(),
+        "rope_base": s.rope_base,
+        "causal": s.causal,
+    }
+
+
+def random_inputs(rng, batch, q_len, n_heads, d_c, d_rope, d_nope, d_v, seqlens,
+                  page_size, shuffle=True, scale=None, base=10000.0, causal=True):
+    """Small fp64 inputs drawn directly (for oracle self-tests)."""
+    seqlens = np.asarray(seqlens)
+    n_pages_seq = (seqlens + page_size - 1) // page_size
+    needed = int(n_pages_seq.sum())
+    num_pages = needed + 2
+    perm = rng.permutation(num_pages) if shuffle else np.arange(num_pages)
+    max_pages = max(1, int(n_pages_seq.max()))
+    table = np.full((batch, max_pages), perm[-1], dtype=np.int64)
+    off = 0
+    for b in range(batch):
+        k = int(n_pages_seq[b])
+        table[b, :k] = perm[off:off + k]
+        off += k
+    return {
+        "q_nope": rng.standard_normal((batch, q_len, n_heads, d_nope)),
+        "q_rope": rng.standard_normal((batch, q_len, n_heads, d_rope)),
+        "w_uk": rng.standard_normal((n_heads, d_nope, d_c)) / np.sqrt(d_c),
+        "w_uv": rng.standard_normal((n_heads, d_v, d_c)) / np.sqrt(d_c),
+        "kv_latent": rng.standard_normal((num_pages, page_size, d_c)),
+        "kv_rope": rng.standard_normal((num_pages, page_size, d_rope)),
+        "block_table": table,
+        "seqlens": seqlens,
+        "page_size": page_size,
+        "softmax_scale": (1.0 / np.sqrt(d_nope + d_rope)) if scale is None else scale,
+        "rope_base": base,
+        "causal": causal,
+    }
