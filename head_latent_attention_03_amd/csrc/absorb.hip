@@ -1,0 +1,216 @@
+// Query absorption and rotary embedding of the decoupled query, gfx950.
+//
+//   q~[m, h, :]  = W_UK[h]^T q^C[m, h, :]      (W^UK absorbed into the query
+//                  side: "Multi-Head Latent Attention: Scaling LLM Serving
+//                  Throughput via Low-Rank KV Compression", section "Empirical
+//                  Gains", paragraph on absorption)
+//   q_pe[m, h, :] = R(pos_m) q^R[m, h, :]      (decoupled RoPE, same section;
+//                  adjacent pairs (x_2i, x_2i+1) rotated by pos * base^(-2i/d_R)
+//                  as on the rotary page "Deepseek-V3 Define 1: Higher
+//                  Attachment of Head", in FP32 as "Multi-Head Latent Attention
+//                  – Latent KV-Cache (DeepSeek v3)" prescribes for RoPE)
+// where m = (b, j) and pos_m = seqlens[b] - q_len + j.
+#include "mla_common.hpp"
+#include "mla_internal.hpp"
+
+namespace mla {
+namespace {
+
+// Rotation of one adjacent pair; the angle is formed in fp64 (pos * theta can
+// reach 6.5e4 rad) and the rotation itself runs in fp32.
+__device__ __forceinline__ void rope_pair(float x0, float x1, int pos, int i, int d_rope,
+                                          float base, float& y0, float& y1) {
+  const double theta = pow((double)base, -2.0 * (double)i / (double)d_rope);
+  double sd, cd;
+  sincos((double)pos * theta, &sd, &cd);
+  const float c = (float)cd, s = (float)sd;
+  y0 = x0 * c - x1 * s;
+  y1 = x0 * s + x1 * c;
+}
+
+// ---------------------------------------------------------------------------
+// bf16 (d_nope = 128, d_lat = 512): one workgroup per (head h, 64 rows m).
+// W_UK[h] [128 x 512] bf16 is staged in LDS (128 KiB) and read as the A
+// operand of D^T = W_UK[h]^T q^C^T with the LDS transpose read; q^C rows are
+// the B operand straight from global memory.  The fp8 variant quantises each
+// q~ row to e4m3 with scale max|q~| / 448.
+constexpr int AB_M = 64;
+constexpr int AB_K = 128;    // d_nope
+constexpr int AB_N = 512;    // d_lat
+
+template <bool FP8>
+__global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_w[AB_K * AB_N];
+  __shared__ float s_amax[4][AB_M];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int nmb = (a.batch * a.q_len + AB_M - 1) / AB_M;
+  const int blk = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int h = blk / nmb;
+  const int mb = blk % nmb;
+  const int m_total = a.batch * a.q_len;
+
+  // stage W_UK[h] (row k = content coordinate, 512 latent columns)
+  const uint16_t* W = (const uint16_t*)a.w_uk + (int64_t)h * AB_K * AB_N;
+  for (int i = threadIdx.x; i < AB_K * AB_N / 8; i += 256)
+    *(u32x4*)&s_w[i * 8] = *(const u32x4*)&W[i * 8];
+
+  // rotary part: 64 rows x d_rope/2 pairs
+  for (int idx = threadIdx.x; idx < AB_M * (a.d_rope / 2); idx += 256) {
+    const int ml = idx / (a.d_rope / 2), i = idx % (a.d_rope / 2);
+    const int m = mb * AB_M + ml;
+    if (m >= m_total) continue;
+    const int b = m / a.q_len, j = m % a.q_len;
+    const int pos = a.seqlens[b] - a.q_len + j;
+    const int64_t off = ((int64_t)m * a.n_heads + h) * a.d_rope + 2 * i;
+    const uint16_t* qr = (const uint16_t*)a.q_rope + off;
+    float y0, y1;
+    rope_pair(bf16_bits_to_f32(qr[0]), bf16_bits_to_f32(qr[1]), pos, i, a.d_rope, a.rope_base,
+              y0, y1);
+    *(uint32_t*)((uint16_t*)a.q_pe + off) = pack_bf16x2(y0, y1);
+  }
+
+  // B operand: q^C rows (m = lr within 16-row block y), k = kk*32 + lg*8 ..
+  u16x8 qb[4][AB_K / 32];
+#pragma unroll
+  for (int y = 0; y < 4; ++y) {
+    const int m = mb * AB_M + y * 16 + lr;
+    const bool valid = m < m_total;
+    const uint16_t* q = (const uint16_t*)a.q_nope + ((int64_t)(valid ? m : 0) * a.n_heads + h) * AB_K;
+#pragma unroll
+    for (int kk = 0; kk < AB_K / 32; ++kk) {
+      const u16x8 v = *(const u16x8*)(q + kk * 32 + lg * 8);
+      qb[y][kk] = valid ? v : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  __syncthreads();
+
+  // wave w: output columns n in [128w, 128w + 128) = 8 blocks of 16
+  f32x4 acc[8][4];
+#pragma unroll
+  for (int x = 0; x < 8; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < AB_K / 32; ++kk) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      // A[m' = n][k] = W[k][n]: lane (lg, lr) addresses W row kk*32 + lg*8 + lr/4
+      // (+4 for the second half), columns n0 + (lr&3)*4 .. +3
+      const int n0 = w * 128 + x * 16;
+      const MLA_LDS uint8_t* p =
+          (const MLA_LDS uint8_t*)s_w +
+          ((kk * 32 + lg * 8 + (lr >> 2)) * AB_N + n0 + (lr & 3) * 4) * 2;
+      const u16x4 lo = lds_read_tr16(p);
+      const u16x4 hi = lds_read_tr16(p + 4 * AB_N * 2);
+      const u16x8 av = u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int y = 0; y < 4; ++y) acc[x][y] = mfma_bf16_16x16x32(av, qb[y][kk], acc[x][y]);
+    }
+  }
+  // lane holds q~^T[n = n0 + lg*4 + r][m = y*16 + lr]
+  if constexpr (!FP8) {
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int m = mb * AB_M + y * 16 + lr;
+      if (m >= m_total) continue;
+      uint16_t* o = (uint16_t*)a.q_lat + ((int64_t)m * a.n_heads + h) * AB_N;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int n = w * 128 + x * 16 + lg * 4;
+        *(u32x2*)(o + n) = u32x2{pack_bf16x2(acc[x][y][0], acc[x][y][1]),
+                                 pack_bf16x2(acc[x][y][2], acc[x][y][3])};
+      }
+    }
+  } else {
+    // row amax over all 512 columns: lanes -> waves -> LDS
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      float mx = 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[x][y][r]));
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      if (lg == 0) s_amax[w][y * 16 + lr] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int ml = y * 16 + lr;
+      const int m = mb * AB_M + ml;
+      const float amax = fmaxf(fmaxf(s_amax[0][ml], s_amax[1][ml]), fmaxf(s_amax[2][ml], s_amax[3][ml]));
+      const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
+      const float inv = 1.0f / sc;
+      if (m >= m_total) continue;
+      uint8_t* o = (uint8_t*)a.q_lat + ((int64_t)m * a.n_heads + h) * AB_N;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int n = w * 128 + x * 16 + lg * 4;
+        int pk = 0;
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = fminf(fmaxf(acc[x][y][r] * inv, -448.f), 448.f);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], pk, false);
+        pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
+        *(int*)(o + n) = pk;
+      }
+      if (w == 0 && lg == 0) a.q_lat_scale[(int64_t)m * a.n_heads + h] = sc;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// f32 (small shapes): one thread per output element.
+__global__ __launch_bounds__(256) void absorb_f32_kernel(AbsorbArgs a) {
+  const int64_t total_lat = (int64_t)a.batch * a.q_len * a.n_heads * a.d_lat;
+  const int64_t total_pe = (int64_t)a.batch * a.q_len * a.n_heads * (a.d_rope / 2);
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx < total_lat) {
+    const int n = (int)(idx % a.d_lat);
+    const int64_t mh = idx / a.d_lat;
+    const int h = (int)(mh % a.n_heads);
+    const float* q = (const float*)a.q_nope + mh * a.d_nope;
+    const float* W = (const float*)a.w_uk + (int64_t)h * a.d_nope * a.d_lat + n;
+    float s = 0.f;
+    for (int k = 0; k < a.d_nope; ++k) s = fmaf(q[k], W[(int64_t)k * a.d_lat], s);
+    ((float*)a.q_lat)[idx] = s;
+  } else if (idx < total_lat + total_pe) {
+    const int64_t p = idx - total_lat;
+    const int i = (int)(p % (a.d_rope / 2));
+    const int64_t mh = p / (a.d_rope / 2);
+    const int64_t m = mh / a.n_heads;
+    const int b = (int)(m / a.q_len), j = (int)(m % a.q_len);
+    const int pos = a.seqlens[b] - a.q_len + j;
+    const float* qr = (const float*)a.q_rope + mh * a.d_rope + 2 * i;
+    float y0, y1;
+    rope_pair(qr[0], qr[1], pos, i, a.d_rope, a.rope_base, y0, y1);
+    float* o = (float*)a.q_pe + mh * a.d_rope + 2 * i;
+    o[0] = y0;
+    o[1] = y1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_absorb_bf16(const AbsorbArgs& a, bool fp8_out, hipStream_t s) {
+  const int nmb = (a.batch * a.q_len + AB_M - 1) / AB_M;
+  const unsigned grid = (unsigned)(nmb * a.n_heads);
+  if (grid == 0) return hipSuccess;
+  if (fp8_out)
+    hipLaunchKernelGGL(absorb_bf16_kernel<true>, dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(absorb_bf16_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_f32(const AbsorbArgs& a, hipStream_t s) {
+  const int64_t total = (int64_t)a.batch * a.q_len * a.n_heads * (a.d_lat + a.d_rope / 2);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(absorb_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

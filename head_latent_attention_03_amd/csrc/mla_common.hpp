@@ -1,0 +1,167 @@
+// Shared device/host definitions of the gfx950 MLA decode library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+// ---------------------------------------------------------------------------
+// vector types (integer lanes for bf16/fp8 payloads; __bf16 vectors only at the
+// MFMA boundary)
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
+typedef __attribute__((ext_vector_type(4))) uint16_t u16x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+#define MLA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Fixed geometry of the bf16/fp8 decode kernels.
+constexpr int kTile = 32;          // cached tokens per pipeline stage
+constexpr int kRowsPerWG = 128;    // (query token, head) rows per workgroup
+constexpr int kWaves = 4;
+constexpr int kPage = 64;
+
+// ---------------------------------------------------------------------------
+// The split plan, recomputed identically by the decode and combine kernels
+// from the device seqlens (no host round trip).
+//
+// Work unit u = (b, rg): sequence b, row group rg of kRowsPerWG rows of the
+// flattened (query token j, head h) space, rows r = j * n_heads + h.  Unit u
+// has tiles_u = ceil(L_b / kTile) tiles of cached tokens; NT = sum of tiles_u.
+// For a target of G workgroups, unit u is cut into
+//     s_u = min(tiles_u, max(1, floor(G * tiles_u / NT)))
+// chunks of near-equal tile counts (none if tiles_u = 0); chunk c covers tiles
+// [c * tiles_u / s_u, (c + 1) * tiles_u / s_u).  Chunks are numbered in unit
+// order (b-major, rg minor); chunk number = workgroup = partial slot.  At most
+// G + (number of units) chunks exist.
+__host__ __device__ inline int tiles_of(int len) { return (len + kTile - 1) / kTile; }
+
+__host__ __device__ inline int plan_splits(int tiles_u, int64_t nt, int G) {
+  if (tiles_u <= 0) return 0;
+  const int64_t s = (int64_t)G * tiles_u / nt;
+  return s < 1 ? 1 : (s > tiles_u ? tiles_u : (int)s);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs.  Give consecutive
+// logical ids to workgroups of one XCD so neighbouring chunks (e.g. the chunks
+// of both row groups of one sequence) share an L2 and run at the same time.
+__device__ inline int xcd_logical_id(int block, int nblocks) {
+  if (nblocks % 8 != 0) return block;
+  return (block % 8) * (nblocks / 8) + block / 8;
+}
+
+// ---------------------------------------------------------------------------
+__device__ inline float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+__device__ inline float wave_sum_xor(float v, int mask) {
+  return v + __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Scalar (SMEM) load of a wave-uniform int, with its wait in the same asm
+// block.  Used for block-table lookups inside pipelined loops: a vector load
+// there would make the compiler drain every outstanding global->LDS copy.
+__device__ __forceinline__ int sload_i32(const int32_t* base, int idx) {
+  int v;
+  asm volatile("s_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
+               : "=s"(v)
+               : "s"(base), "s"(idx * 4)
+               : "memory");
+  return v;
+}
+
+// Total tiles NT over all units (every lane gets the same value).
+__device__ inline int64_t plan_total_tiles(const int32_t* seqlens, int batch, int row_groups,
+                                           int lane) {
+  int part = 0;
+  for (int b = lane; b < batch; b += 64) part += tiles_of(seqlens[b]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+  return (int64_t)uni(part) * row_groups;
+}
+
+// Chunks of all units of sequences [0, b_end) (the first chunk number of b_end).
+__device__ inline int plan_chunks_before(const int32_t* seqlens, int b_end, int row_groups,
+                                         int64_t nt, int G, int lane) {
+  int part = 0;
+  for (int b = lane; b < b_end; b += 64)
+    part += plan_splits(tiles_of(seqlens[b]), nt, G) * row_groups;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+  return uni(part);
+}
+
+struct Chunk {
+  int b, rg, c, splits, tiles, len;
+};
+
+// The chunk numbered g; false if g is past the last chunk.
+__device__ inline bool plan_find_chunk(const int32_t* seqlens, int batch, int row_groups,
+                                       int64_t nt, int G, int g, int lane, Chunk& out) {
+  int base = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int b = b0 + lane;
+    const int cnt = (b < batch) ? plan_splits(tiles_of(seqlens[b]), nt, G) * row_groups : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const int o = __shfl_up(incl, m, 64);
+      if (lane >= m) incl += o;
+    }
+    const uint64_t hit = __ballot(base + incl > g);
+    if (hit) {
+      const int f = uni(__builtin_ctzll(hit));
+      const int start = base + uni(__shfl(incl - cnt, f, 64));
+      out.b = uni(b0 + f);
+      out.len = uni(seqlens[out.b]);
+      out.tiles = tiles_of(out.len);
+      out.splits = plan_splits(out.tiles, nt, G);
+      const int off = g - start;
+      out.rg = off / out.splits;
+      out.c = off % out.splits;
+      return true;
+    }
+    base += uni(__shfl(incl, 63, 64));
+  }
+  return false;
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ inline float bf16_bits_to_f32(uint16_t u) {
+  return __uint_as_float(((uint32_t)u) << 16);
+}
+
+__device__ inline f32x4 mfma_bf16_16x16x32(u16x8 a, u16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// LDS transpose read: in each group of 16 lanes, lane n receives column n of
+// the 4 x 16 block of 16-bit elements whose row r, columns 4q..4q+3 are
+// addressed by lane 4r + q of that group.
+__device__ inline u16x4 lds_read_tr16(const MLA_LDS uint8_t* p) {
+  i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MLA_LDS i16x4*)p);
+  return __builtin_bit_cast(u16x4, v);
+}
+
+// 16-byte global -> LDS copy: lane l's 16 bytes land at lds_base + 16 * l.
+__device__ inline void dma16(const void* gsrc, MLA_LDS uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (MLA_LDS void*)lds_base, 16, 0, 0);
+}
+
+}  // namespace mla

@@ -1,0 +1,61 @@
+// Launch arguments passed from the C ABI layer to the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+
+struct AbsorbArgs {
+  const void* q_nope;
+  const void* q_rope;
+  const int32_t* seqlens;
+  const void* w_uk;
+  void* q_lat;
+  float* q_lat_scale;
+  void* q_pe;
+  int32_t batch, q_len, n_heads, d_nope, d_lat, d_rope;
+  float rope_base;
+};
+
+struct DecodeArgs {
+  const void* q_lat;
+  const float* q_scale;      // fp8 latent only
+  const void* q_pe;
+  const void* kv_lat;
+  const float* kv_scale;     // fp8 latent only
+  const void* kv_rope;
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  float* part_o;             // [slots, 128, d_lat] f32
+  float* part_lse;           // [slots, 128]        f32 (natural log)
+  float* part_tmp;           // [slots, 128, d_lat] f32 scratch for mid-chunk merges
+  int32_t max_pages, batch, q_len, n_heads, causal;
+  int32_t d_lat, d_rope;
+  int32_t num_wg, row_groups;
+  float scale_log2;          // softmax_scale * log2(e)
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* seqlens;
+  const void* w_uv;          // may be null
+  void* out;
+  float* lse;                // may be null
+  int32_t batch, q_len, n_heads, d_lat, d_v;
+  int32_t num_wg, row_groups;
+  int32_t out_dtype;         // Dt
+};
+
+hipError_t launch_absorb_bf16(const AbsorbArgs& a, bool fp8_out, hipStream_t s);
+hipError_t launch_absorb_f32(const AbsorbArgs& a, hipStream_t s);
+// grid = launched workgroups (an upper bound of the plan's chunk count)
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, int grid);
+hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t s, int grid);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s, int grid);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace mla
