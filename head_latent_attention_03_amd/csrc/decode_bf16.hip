@@ -25,13 +25,18 @@
 //     the next product, so the probabilities never touch LDS.
 //   * O^T += C^T P^T with the same MFMA: A = C^T read with ds_read_b64_tr_b16
 //     (the LDS transpose read), B = P from registers.
+//   * The HBM -> LDS copies are issued from inline asm (see dma16), so the
+//     compiler schedules the LDS reads freely; the ring is guarded by explicit
+//     vmcnt waits and one barrier per tile.
 //   * Online softmax in fp32 (base 2, scale folded).  Each row keeps a fixed
-//     reference maximum instead of rescaling the accumulator every time the
-//     maximum grows: probabilities are exp2(s - m_ref) <= 2^64, so nothing
-//     overflows.  If a tile's maximum exceeds m_ref + 64, the accumulated part
-//     is merged into the row's partial slot (log-sum-exp weights) and the
-//     accumulator restarts at the new reference.  The accumulator is thus
-//     only ever written by MFMAs, which keeps it resident in AGPRs.
+//     reference maximum, set by its first scores, instead of rescaling the
+//     accumulator whenever the maximum grows: probabilities are
+//     exp2(s - m_ref) <= 2^64, so nothing overflows, and no cross-lane
+//     traffic is needed while scores stay below m_ref + 64.  If a wave sees a
+//     score above that, it finishes the pass, takes the true row maxima as
+//     references and runs its chunk once more from a private LDS stage.  The
+//     accumulator is thus only ever written by MFMAs, which keeps it resident
+//     in AGPRs.
 //   * LDS rows are XOR-swizzled on 16-byte chunks (chunk c of token t is
 //     stored at c ^ (t & 7)) so both read patterns spread over the banks.
 #include "mla_common.hpp"
@@ -95,46 +100,17 @@ __device__ __forceinline__ void wait_tiles(int remaining_after) {
   else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Eight LDS transpose reads (4 column blocks x the two 16-token halves) and a
-// wait for them, in one asm block.  Written as asm because the compiler cannot
-// tell that these reads never touch the stages the DMA is still filling, and
-// would otherwise drain every outstanding global->LDS copy before each read.
-template <int OFF>
-__device__ __forceinline__ void tr_read4(const MLA_LDS uint8_t* p0, const MLA_LDS uint8_t* p1,
-                                         const MLA_LDS uint8_t* p2, const MLA_LDS uint8_t* p3,
-                                         u32x2 (&r)[8]) {
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]),
-        "=&v"(r[6]), "=&v"(r[7])
-      : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "i"(OFF), "i"(OFF + 16 * LAT_ROW)
-      : "memory");
-}
-
 struct SegState {
   u16x8 q[2][KS];       // absorbed query (B operand), per 16-row block
   f32x4 o[2][DB];       // O^T accumulator: lane holds head lr, 4 latent dims
   float m[2], l[2];     // reference max (log2 units, scaled) and per-lane sum
   int lim[2];           // keys visible to the lane's row: t < lim
-  bool dumped;          // the slot already holds an earlier part of this chunk
+  float tmax[2];        // largest score this lane has seen (log2 units, scaled)
+  bool redo;            // a score passed m_ref + 64 with mass already accumulated
 };
 
-// Bank the accumulated part of the chunk in its partial slot.
-// The slot holds the chunk's output so far, normalised, and its natural-log
-// log-sum-exp.  The first time, the slot receives O / l directly.  Later
-// times (a row's scores jumped far above its reference mid-chunk) the raw
-// accumulator is stored to the slot's scratch rows first and read back, so
-// the merge arithmetic runs on loaded copies and the accumulator itself is
-// only ever touched by MFMAs and stores.
-__device__ __forceinline__ void flush_to_slot(const DecodeArgs& a, SegState& S, int64_t slot,
+// The chunk's partial: o~ / l and its natural-log log-sum-exp.
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, SegState& S, int64_t slot,
                                               int w, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
@@ -142,42 +118,18 @@ __device__ __forceinline__ void flush_to_slot(const DecodeArgs& a, SegState& S, 
     float lsum = S.l[hb];
     lsum = wave_sum_xor(lsum, 16);
     lsum = wave_sum_xor(lsum, 32);
-    const float lse_c = lsum > 0.f ? (S.m[hb] + __log2f(lsum)) * kLn2 : -INFINITY;
+    const float lse = lsum > 0.f ? (S.m[hb] + __log2f(lsum)) * kLn2 : -INFINITY;
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
     const int row = w * 32 + hb * 16 + lr;
     float* dst = a.part_o + (slot * kRowsPerWG + row) * D_LAT + lg * 4;
-    float* lse_dst = a.part_lse + slot * kRowsPerWG + row;
-    if (!S.dumped) {
-      const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) *(f32x4*)(dst + db * 16) = S.o[hb][db] * inv;
-      if (lg == 0) *lse_dst = lse_c;
-    } else {
-      float* tmp = a.part_tmp + (slot * kRowsPerWG + row) * D_LAT + lg * 4;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) *(f32x4*)(tmp + db * 16) = S.o[hb][db];
-      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
-      const float lse_d = *lse_dst;
-      const float mx = fmaxf(lse_d, lse_c);
-      const float wd = (lse_d == -INFINITY) ? 0.f : __expf(lse_d - mx);
-      const float wc = (lse_c == -INFINITY) ? 0.f : __expf(lse_c - mx);
-      const float tot = wd + wc;
-      const float fd = tot > 0.f ? wd / tot : 0.f;
-      const float fc = (tot > 0.f && lsum > 0.f) ? wc / (tot * lsum) : 0.f;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        f32x4 prev = *(const f32x4*)(dst + db * 16);
-        if (fd == 0.f) prev = f32x4{0.f, 0.f, 0.f, 0.f};   // the slot may hold garbage
-        const f32x4 cur = *(const f32x4*)(tmp + db * 16);
-        *(f32x4*)(dst + db * 16) = prev * fd + cur * fc;
-      }
-      if (lg == 0) *lse_dst = tot > 0.f ? mx + __logf(tot) : -INFINITY;
-    }
+    for (int db = 0; db < DB; ++db) *(f32x4*)(dst + db * 16) = S.o[hb][db] * inv;
+    if (lg == 0) a.part_lse[slot * kRowsPerWG + row] = lse;
   }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent");
 }
 
-__device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, int64_t slot,
-                                             int st, int tok0, int w, int lane) {
+__device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, int st, int tok0,
+                                             int lane) {
   const int lr = lane & 15, lg = lane >> 4;
   const MLA_LDS uint8_t* lat = stage_base(st);
   const MLA_LDS uint8_t* rope = lat + LAT_STAGE;
@@ -216,13 +168,17 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
       sacc[0][hb] = mfma_bf16_16x16x32(cur0, S.q[hb][kk], sacc[0][hb]);
       sacc[1][hb] = mfma_bf16_16x16x32(cur1, S.q[hb][kk], sacc[1][hb]);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // ---- online softmax; lane holds head (hb*16 + lr), tokens tb*16 + lg*4 + r
+  // Common path: every score is below its row's reference + 64, so the
+  // probabilities follow with no cross-lane traffic.  Otherwise (the row's
+  // first scores, or a jump) the row maximum is formed across the row's four
+  // lanes and the reference moves, banking what was accumulated if needed.
   float sv[2][2][4];
-  float mt[2];
-  bool need[2];
-  bool dump = false;
+  float lmax[2];
+  bool need_lane = false;
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     float mx = -INFINITY;
@@ -235,35 +191,30 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
         sv[hb][tb][r] = v;
         mx = fmaxf(mx, v);
       }
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    mt[hb] = mx;
-    need[hb] = mx > S.m[hb] + kRefSlack;
-    dump |= need[hb] && (S.l[hb] > 0.f);
+    lmax[hb] = mx;
+    S.tmax[hb] = fmaxf(S.tmax[hb], mx);
+    need_lane |= mx > S.m[hb] + kRefSlack;
   }
-  if (__ballot(dump)) {
-    // rare: a row's scores jumped far above its reference; bank what has
-    // been accumulated and restart from the new reference
-    if (!S.dumped) {
-      // an empty slot merges as log-sum-exp -inf
-      if (lg == 0) {
-        a.part_lse[slot * kRowsPerWG + w * 32 + lr] = -INFINITY;
-        a.part_lse[slot * kRowsPerWG + w * 32 + 16 + lr] = -INFINITY;
-      }
-      S.dumped = true;
-    }
-    flush_to_slot(a, S, slot, w, lane);
+  if (__ballot(need_lane)) {
+    // a row's first scores set its reference; a later jump marks the wave
+    // for a second pass with the true maxima
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-#pragma unroll
-      for (int db = 0; db < DB; ++db) S.o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-      S.l[hb] = 0.f;
+      float mx = lmax[hb];
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      float mass = S.l[hb];
+      mass = wave_sum_xor(mass, 16);
+      mass = wave_sum_xor(mass, 32);
+      const bool need = mx > S.m[hb] + kRefSlack;
+      if (need && mass == 0.f) S.m[hb] = mx;
+      S.redo |= need && mass > 0.f;
     }
+    S.redo = __ballot(S.redo) != 0;
   }
   u16x8 pf[2];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    if (need[hb]) S.m[hb] = mt[hb];
     const float mref = S.m[hb];
     uint32_t pk[4];
     float psum = 0.f;
@@ -271,8 +222,9 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
     for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
       for (int r = 0; r < 4; r += 2) {
-        const float p0 = (mref == -INFINITY) ? 0.f : exp2f(sv[hb][tb][r] - mref);
-        const float p1 = (mref == -INFINITY) ? 0.f : exp2f(sv[hb][tb][r + 1] - mref);
+        // (the clamp only matters in a pass that will be redone)
+        const float p0 = (mref == -INFINITY) ? 0.f : exp2f(fminf(sv[hb][tb][r] - mref, kRefSlack));
+        const float p1 = (mref == -INFINITY) ? 0.f : exp2f(fminf(sv[hb][tb][r + 1] - mref, kRefSlack));
         const uint32_t u = pack_bf16x2(p0, p1);
         pk[tb * 2 + r / 2] = u;
         psum += __uint_as_float(u << 16) + __uint_as_float(u & 0xffff0000u);
@@ -288,31 +240,25 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
   const int f1 = t1 & 7;
   const int cbit = (lr & 3) >> 1;
   const int half = (lr & 1) << 3;
-  const MLA_LDS uint8_t* p0 = lat + t1 * LAT_ROW + (((0 + cbit) ^ f1) << 4) + half;
-  const MLA_LDS uint8_t* p1 = lat + t1 * LAT_ROW + (((2 + cbit) ^ f1) << 4) + half;
-  const MLA_LDS uint8_t* p2 = lat + t1 * LAT_ROW + (((4 + cbit) ^ f1) << 4) + half;
-  const MLA_LDS uint8_t* p3 = lat + t1 * LAT_ROW + (((6 + cbit) ^ f1) << 4) + half;
+  const MLA_LDS uint8_t* pv_base[4];
 #pragma unroll
-  for (int bat = 0; bat < DB / 4; ++bat) {
-    u32x2 r[8];
-    switch (bat) {
-      case 0: tr_read4<0 * 128>(p0, p1, p2, p3, r); break;
-      case 1: tr_read4<1 * 128>(p0, p1, p2, p3, r); break;
-      case 2: tr_read4<2 * 128>(p0, p1, p2, p3, r); break;
-      case 3: tr_read4<3 * 128>(p0, p1, p2, p3, r); break;
-      case 4: tr_read4<4 * 128>(p0, p1, p2, p3, r); break;
-      case 5: tr_read4<5 * 128>(p0, p1, p2, p3, r); break;
-      case 6: tr_read4<6 * 128>(p0, p1, p2, p3, r); break;
-      default: tr_read4<7 * 128>(p0, p1, p2, p3, r); break;
-    }
+  for (int v = 0; v < 4; ++v)
+    pv_base[v] = lat + t1 * LAT_ROW + (((2 * v + cbit) ^ f1) << 4) + half;
+  auto load_c = [&](int db) -> u16x8 {
+    const MLA_LDS uint8_t* p = pv_base[db & 3] + (db >> 2) * 128;
+    const u16x4 lo = lds_read_tr16(p);
+    const u16x4 hi = lds_read_tr16(p + 16 * LAT_ROW);
+    return u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+  u16x8 c0 = load_c(0), c1 = load_c(1);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int db = bat * 4 + v;
-      const u16x8 av = __builtin_bit_cast(u16x8, u32x4{r[2 * v][0], r[2 * v][1],
-                                                       r[2 * v + 1][0], r[2 * v + 1][1]});
+  for (int db = 0; db < DB; ++db) {
+    const u16x8 av = c0;
+    c0 = c1;
+    if (db + 2 < DB) c1 = load_c(db + 2);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) S.o[hb][db] = mfma_bf16_16x16x32(av, pf[hb], S.o[hb][db]);
-    }
+    for (int hb = 0; hb < 2; ++hb) S.o[hb][db] = mfma_bf16_16x16x32(av, pf[hb], S.o[hb][db]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -359,7 +305,8 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     S.l[hb] = 0.f;
     S.lim[hb] = valid ? (a.causal ? ch.len - a.q_len + j + 1 : ch.len) : 0;
   }
-  S.dumped = false;
+  S.redo = false;
+  S.tmax[0] = S.tmax[1] = -INFINITY;
 
   // prologue: three tiles in flight (issued after the query loads, so the
   // first wait below covers both)
@@ -372,9 +319,33 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     if (i + 3 < n) issue_tile(a, ch.b, ch.len, k0 + i + 3, (i + 3) & 3, w, lane);
-    compute_tile(a, S, slot, i & 3, (k0 + i) * kTile, w, lane);
+    compute_tile(a, S, i & 3, (k0 + i) * kTile, lane);
   }
-  flush_to_slot(a, S, slot, w, lane);
+
+  // rare second pass of this wave, from its own stage (all waves are past
+  // the ring once the barrier completes)
+  __builtin_amdgcn_s_barrier();
+  if (S.redo) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      float mx = S.tmax[hb];
+      mx = wave_max_xor(mx, 16);
+      mx = wave_max_xor(mx, 32);
+      S.m[hb] = mx;
+      S.l[hb] = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) S.o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    S.redo = false;
+    for (int i = 0; i < n; ++i) {
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) issue_tile(a, ch.b, ch.len, k0 + i, w, ww, lane);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      compute_tile(a, S, w, (k0 + i) * kTile, lane);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+  }
+  write_partial(a, S, slot, w, lane);
 }
 
 }  // namespace

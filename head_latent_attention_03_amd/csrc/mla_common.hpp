@@ -159,9 +159,20 @@ __device__ inline u16x4 lds_read_tr16(const MLA_LDS uint8_t* p) {
   return __builtin_bit_cast(u16x4, v);
 }
 
-// 16-byte global -> LDS copy: lane l's 16 bytes land at lds_base + 16 * l.
-__device__ inline void dma16(const void* gsrc, MLA_LDS uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (MLA_LDS void*)lds_base, 16, 0, 0);
+// 16-byte global -> LDS copy: lane l's 16 bytes land at lds_base + 16 * l
+// (lds_base is wave-uniform).  Written as asm so that the compiler's memory
+// model does not see it: otherwise any LDS read it cannot prove disjoint from
+// the copy's destination gets a wait for every outstanding VMEM operation.
+// The copy has no register result; callers wait for it explicitly with
+// s_waitcnt vmcnt before a barrier, and no compiler-visible VMEM load of the
+// same wave may rely on a vmcnt count made while a copy is outstanding other
+// than a conservative one (the compiler under-counts, which over-waits).
+__device__ __forceinline__ void dma16(const void* gsrc, const MLA_LDS uint8_t* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(m0), "v"(gsrc)
+               : "memory", "m0");
 }
 
 }  // namespace mla

@@ -240,3 +240,30 @@ def mla_decode_absorbed(inputs, rows=None, return_probs=False):
     Used only to check absorption is exact ([LRKV] "Empirical Gains"; [SNAP]).
     """
     return _decode(inputs, rows, return_probs, absorbed=True)
+
+
+def inputs_from_workload(wl, latent_override=None):
+    """Decode a generated workload's stored arrays into this module's fp64 inputs.
+
+    ``wl`` is any object with the generator's fields (spec, kv_latent,
+    kv_scale, kv_rope, q_nope, q_rope, w_uk, w_uv, block_table, seqlens); the
+    oracle reads only those stored bits, through its own codecs.
+    """
+    s = wl.spec
+    lat = latent_override
+    if lat is None:
+        lat = decode_stored(wl.kv_latent, s.latent_dtype, wl.kv_scale)
+    return {
+        "q_nope": decode_stored(wl.q_nope, s.act_dtype),
+        "q_rope": decode_stored(wl.q_rope, s.act_dtype),
+        "w_uk": decode_stored(wl.w_uk, s.act_dtype),
+        "w_uv": decode_stored(wl.w_uv, s.act_dtype),
+        "kv_latent": lat,
+        "kv_rope": decode_stored(wl.kv_rope, s.act_dtype),
+        "block_table": np.asarray(wl.block_table),
+        "seqlens": np.asarray(wl.seqlens),
+        "page_size": s.page_size,
+        "softmax_scale": s.scale(),
+        "rope_base": s.rope_base,
+        "causal": s.causal,
+    }

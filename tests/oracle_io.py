@@ -6,24 +6,7 @@ import oracle
 
 
 def oracle_inputs(wl, latent_override=None):
-    s = wl.spec
-    lat = latent_override
-    if lat is None:
-        lat = oracle.decode_stored(wl.kv_latent, s.latent_dtype, wl.kv_scale)
-    return {
-        "q_nope": oracle.decode_stored(wl.q_nope, s.act_dtype),
-        "q_rope": oracle.decode_stored(wl.q_rope, s.act_dtype),
-        "w_uk": oracle.decode_stored(wl.w_uk, s.act_dtype),
-        "w_uv": oracle.decode_stored(wl.w_uv, s.act_dtype),
-        "kv_latent": lat,
-        "kv_rope": oracle.decode_stored(wl.kv_rope, s.act_dtype),
-        "block_table": np.asarray(wl.block_table),
-        "seqlens": np.asarray(wl.seqlens),
-        "page_size": s.page_size,
-        "softmax_scale": s.scale(),
-        "rope_base": s.rope_base,
-        "causal": s.causal,
-    }
+    return oracle.inputs_from_workload(wl, latent_override)
 
 
 def random_inputs(rng, batch, q_len, n_heads, d_c, d_rope, d_nope, d_v, seqlens,
