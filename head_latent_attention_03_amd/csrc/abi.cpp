@@ -85,7 +85,7 @@ struct Layout {
   int row_groups;
   int num_wg;      // target workgroups G of the split plan
   int grid;        // launched workgroups (>= number of chunks)
-  size_t off_o, off_lse, off_tmp, bytes;
+  size_t off_o, off_lse, off_units, bytes;
 };
 
 Layout layout_for(const mla_dims_t* d, int32_t batch, int32_t q_len, int cus) {
@@ -95,11 +95,12 @@ Layout layout_for(const mla_dims_t* d, int32_t batch, int32_t q_len, int cus) {
   const int64_t units = (int64_t)batch * L.row_groups;
   L.grid = (int)align_up((size_t)(L.num_wg + units), 8);
   const size_t slots = (size_t)L.grid;
-  const size_t o_bytes = slots * mla::kRowsPerWG * (size_t)d->d_latent * 4;
+  const size_t part_elt = d->act_dtype == MLA_F32 ? 4 : 2;
+  const size_t o_bytes = slots * mla::kRowsPerWG * (size_t)d->d_latent * part_elt;
   L.off_o = 0;
   L.off_lse = align_up(o_bytes, 256);
-  L.off_tmp = align_up(L.off_lse + slots * mla::kRowsPerWG * 4, 256);
-  L.bytes = L.off_tmp + o_bytes;
+  L.off_units = align_up(L.off_lse + slots * mla::kRowsPerWG * 4, 256);
+  L.bytes = align_up(L.off_units + (size_t)units * 2 * 4, 256);
   return L;
 }
 
@@ -206,9 +207,9 @@ MLA_EXPORT mla_status_t mla_decode_paged(const mla_dims_t* dims, int32_t batch, 
   a.block_table = block_table;
   a.seqlens = seqlens;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  a.part_o = reinterpret_cast<float*>(ws + L.off_o);
+  a.part_o = ws + L.off_o;
   a.part_lse = reinterpret_cast<float*>(ws + L.off_lse);
-  a.part_tmp = reinterpret_cast<float*>(ws + L.off_tmp);
+  a.unit_chunks = reinterpret_cast<int32_t*>(ws + L.off_units);
   a.max_pages = max_pages_per_seq;
   a.batch = batch;
   a.q_len = q_len;
@@ -253,8 +254,9 @@ MLA_EXPORT mla_status_t mla_combine(const mla_dims_t* dims, int32_t batch, int32
   if (batch == 0) return MLA_OK;
   CombineArgs a;
   const uint8_t* ws = static_cast<const uint8_t*>(workspace);
-  a.part_o = reinterpret_cast<const float*>(ws + L.off_o);
+  a.part_o = ws + L.off_o;
   a.part_lse = reinterpret_cast<const float*>(ws + L.off_lse);
+  a.unit_chunks = reinterpret_cast<const int32_t*>(ws + L.off_units);
   a.seqlens = seqlens;
   a.w_uv = w_uv;
   a.out = out;

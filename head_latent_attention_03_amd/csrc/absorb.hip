@@ -16,59 +16,93 @@
 namespace mla {
 namespace {
 
-// Rotation of one adjacent pair; the angle is formed in fp64 (pos * theta can
-// reach 6.5e4 rad) and the rotation itself runs in fp32.
-__device__ __forceinline__ void rope_pair(float x0, float x1, int pos, int i, int d_rope,
-                                          float base, float& y0, float& y1) {
-  const double theta = pow((double)base, -2.0 * (double)i / (double)d_rope);
-  double sd, cd;
-  sincos((double)pos * theta, &sd, &cd);
-  const float c = (float)cd, s = (float)sd;
+// Rotation of one adjacent pair by pos * theta_i, theta_i = base^(-2i/d_rope).
+// The angle (up to ~6.5e4 rad) is formed and reduced to [-pi, pi] in fp64, so
+// the fp32 sin/cos that follow see a small argument; the rotation runs in
+// fp32.  theta is given in fp64.
+__device__ __forceinline__ void rope_pair(float x0, float x1, int pos, double theta, float& y0,
+                                          float& y1) {
+  constexpr double kTwoPi = 6.283185307179586476925286766559;
+  const double ang = (double)pos * theta;
+  const double red = ang - kTwoPi * rint(ang * (1.0 / kTwoPi));
+  float s, c;
+  sincosf((float)red, &s, &c);
   y0 = x0 * c - x1 * s;
   y1 = x0 * s + x1 * c;
 }
 
+__device__ __forceinline__ double rope_theta(int i, int d_rope, float base) {
+  return exp2(-2.0 * (double)i / (double)d_rope * log2((double)base));
+}
+
 // ---------------------------------------------------------------------------
-// bf16 (d_nope = 128, d_lat = 512): one workgroup per (head h, 64 rows m).
-// W_UK[h] [128 x 512] bf16 is staged in LDS (128 KiB) and read as the A
-// operand of D^T = W_UK[h]^T q^C^T with the LDS transpose read; q^C rows are
-// the B operand straight from global memory.  The fp8 variant quantises each
-// q~ row to e4m3 with scale max|q~| / 448.
+// bf16 (d_nope = 128, d_lat = 512): one workgroup per (head h, NB latent
+// columns, 64 rows m).  The W_UK[h] slice [128 x NB] bf16 is staged in LDS and
+// read as the A operand of D^T = W_UK[h]^T q^C^T with the LDS transpose read;
+// q^C rows are the B operand straight from global memory.  NB = 128 for bf16
+// output (4 column blocks per head, enough workgroups to cover the chip);
+// NB = 512 for e4m3 output, whose per-row scale max|q~| / 448 needs the whole
+// row in one workgroup.
 constexpr int AB_M = 64;
 constexpr int AB_K = 128;    // d_nope
 constexpr int AB_N = 512;    // d_lat
 
-template <bool FP8>
+template <int NB, bool FP8>
 __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_w[AB_K * AB_N];
+  // row pitch NB*2 + 32 bytes: the four rows of a transpose-read group land
+  // on disjoint banks
+  constexpr int PITCH = NB * 2 + 32;
+  constexpr int NBLK = NB / 16 / 4;            // 16-column blocks per wave
+  __shared__ __attribute__((aligned(16))) uint8_t s_w[AB_K * PITCH];
   __shared__ float s_amax[4][AB_M];
+  __shared__ double s_theta[64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int nmb = (a.batch * a.q_len + AB_M - 1) / AB_M;
+  constexpr int NCB = AB_N / NB;               // column blocks per head
   const int blk = xcd_logical_id(blockIdx.x, gridDim.x);
-  const int h = blk / nmb;
+  const int h = blk / (nmb * NCB);
+  const int cb = (blk / nmb) % NCB;
   const int mb = blk % nmb;
   const int m_total = a.batch * a.q_len;
 
-  // stage W_UK[h] (row k = content coordinate, 512 latent columns)
-  const uint16_t* W = (const uint16_t*)a.w_uk + (int64_t)h * AB_K * AB_N;
-  for (int i = threadIdx.x; i < AB_K * AB_N / 8; i += 256)
-    *(u32x4*)&s_w[i * 8] = *(const u32x4*)&W[i * 8];
+  // stage W_UK[h][:, cb*NB .. +NB] (row k = content coordinate); all loads
+  // are issued before the first store
+  const uint16_t* W = (const uint16_t*)a.w_uk + (int64_t)h * AB_K * AB_N + cb * NB;
+  constexpr int CHUNKS = AB_K * NB / 8;        // 16-byte chunks
+  constexpr int PER_T = CHUNKS / 256;
+  u32x4 stage[PER_T];
+#pragma unroll
+  for (int i = 0; i < PER_T; ++i) {
+    const int c = threadIdx.x + i * 256;
+    const int row = c / (NB / 8), col = c % (NB / 8);
+    stage[i] = *(const u32x4*)&W[(int64_t)row * AB_N + col * 8];
+  }
+#pragma unroll
+  for (int i = 0; i < PER_T; ++i) {
+    const int c = threadIdx.x + i * 256;
+    const int row = c / (NB / 8), col = c % (NB / 8);
+    *(u32x4*)&s_w[row * PITCH + col * 16] = stage[i];
+  }
 
-  // rotary part: 64 rows x d_rope/2 pairs
-  for (int idx = threadIdx.x; idx < AB_M * (a.d_rope / 2); idx += 256) {
-    const int ml = idx / (a.d_rope / 2), i = idx % (a.d_rope / 2);
-    const int m = mb * AB_M + ml;
-    if (m >= m_total) continue;
-    const int b = m / a.q_len, j = m % a.q_len;
-    const int pos = a.seqlens[b] - a.q_len + j;
-    const int64_t off = ((int64_t)m * a.n_heads + h) * a.d_rope + 2 * i;
-    const uint16_t* qr = (const uint16_t*)a.q_rope + off;
-    float y0, y1;
-    rope_pair(bf16_bits_to_f32(qr[0]), bf16_bits_to_f32(qr[1]), pos, i, a.d_rope, a.rope_base,
-              y0, y1);
-    *(uint32_t*)((uint16_t*)a.q_pe + off) = pack_bf16x2(y0, y1);
+  // rotary part (column block 0 only): 64 rows x d_rope/2 pairs
+  if (cb == 0) {
+    if (threadIdx.x < a.d_rope / 2 && threadIdx.x < 64)
+      s_theta[threadIdx.x] = rope_theta(threadIdx.x, a.d_rope, a.rope_base);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < AB_M * (a.d_rope / 2); idx += 256) {
+      const int ml = idx / (a.d_rope / 2), i = idx % (a.d_rope / 2);
+      const int m = mb * AB_M + ml;
+      if (m >= m_total) continue;
+      const int b = m / a.q_len, j = m % a.q_len;
+      const int pos = a.seqlens[b] - a.q_len + j;
+      const int64_t off = ((int64_t)m * a.n_heads + h) * a.d_rope + 2 * i;
+      const uint16_t* qr = (const uint16_t*)a.q_rope + off;
+      float y0, y1;
+      rope_pair(bf16_bits_to_f32(qr[0]), bf16_bits_to_f32(qr[1]), pos, s_theta[i], y0, y1);
+      *(uint32_t*)((uint16_t*)a.q_pe + off) = pack_bf16x2(y0, y1);
+    }
   }
 
   // B operand: q^C rows (m = lr within 16-row block y), k = kk*32 + lg*8 ..
@@ -86,50 +120,50 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
   }
   __syncthreads();
 
-  // wave w: output columns n in [128w, 128w + 128) = 8 blocks of 16
-  f32x4 acc[8][4];
+  // wave w: columns n in [w*NB/4, (w+1)*NB/4) of the block = NBLK blocks of 16
+  f32x4 acc[NBLK][4];
 #pragma unroll
-  for (int x = 0; x < 8; ++x)
+  for (int x = 0; x < NBLK; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < AB_K / 32; ++kk) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int x = 0; x < NBLK; ++x) {
       // A[m' = n][k] = W[k][n]: lane (lg, lr) addresses W row kk*32 + lg*8 + lr/4
       // (+4 for the second half), columns n0 + (lr&3)*4 .. +3
-      const int n0 = w * 128 + x * 16;
-      const MLA_LDS uint8_t* p =
-          (const MLA_LDS uint8_t*)s_w +
-          ((kk * 32 + lg * 8 + (lr >> 2)) * AB_N + n0 + (lr & 3) * 4) * 2;
+      const int n0 = (w * NBLK + x) * 16;
+      const MLA_LDS uint8_t* p = (const MLA_LDS uint8_t*)s_w +
+                                 (kk * 32 + lg * 8 + (lr >> 2)) * PITCH + (n0 + (lr & 3) * 4) * 2;
       const u16x4 lo = lds_read_tr16(p);
-      const u16x4 hi = lds_read_tr16(p + 4 * AB_N * 2);
+      const u16x4 hi = lds_read_tr16(p + 4 * PITCH);
       const u16x8 av = u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
       for (int y = 0; y < 4; ++y) acc[x][y] = mfma_bf16_16x16x32(av, qb[y][kk], acc[x][y]);
     }
   }
-  // lane holds q~^T[n = n0 + lg*4 + r][m = y*16 + lr]
+  // lane holds q~^T[n = cb*NB + n0 + lg*4 + r][m = y*16 + lr]
   if constexpr (!FP8) {
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
       const int m = mb * AB_M + y * 16 + lr;
       if (m >= m_total) continue;
-      uint16_t* o = (uint16_t*)a.q_lat + ((int64_t)m * a.n_heads + h) * AB_N;
+      uint16_t* o = (uint16_t*)a.q_lat + ((int64_t)m * a.n_heads + h) * AB_N + cb * NB;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int n = w * 128 + x * 16 + lg * 4;
+      for (int x = 0; x < NBLK; ++x) {
+        const int n = (w * NBLK + x) * 16 + lg * 4;
         *(u32x2*)(o + n) = u32x2{pack_bf16x2(acc[x][y][0], acc[x][y][1]),
                                  pack_bf16x2(acc[x][y][2], acc[x][y][3])};
       }
     }
   } else {
+    static_assert(NB == AB_N, "the e4m3 row scale needs the whole row");
     // row amax over all 512 columns: lanes -> waves -> LDS
 #pragma unroll
     for (int y = 0; y < 4; ++y) {
       float mx = 0.f;
 #pragma unroll
-      for (int x = 0; x < 8; ++x)
+      for (int x = 0; x < NBLK; ++x)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[x][y][r]));
       mx = wave_max_xor(mx, 16);
@@ -147,8 +181,8 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
       if (m >= m_total) continue;
       uint8_t* o = (uint8_t*)a.q_lat + ((int64_t)m * a.n_heads + h) * AB_N;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const int n = w * 128 + x * 16 + lg * 4;
+      for (int x = 0; x < NBLK; ++x) {
+        const int n = (w * NBLK + x) * 16 + lg * 4;
         int pk = 0;
         float v[4];
 #pragma unroll
@@ -186,7 +220,7 @@ __global__ __launch_bounds__(256) void absorb_f32_kernel(AbsorbArgs a) {
     const int pos = a.seqlens[b] - a.q_len + j;
     const float* qr = (const float*)a.q_rope + mh * a.d_rope + 2 * i;
     float y0, y1;
-    rope_pair(qr[0], qr[1], pos, i, a.d_rope, a.rope_base, y0, y1);
+    rope_pair(qr[0], qr[1], pos, rope_theta(i, a.d_rope, a.rope_base), y0, y1);
     float* o = (float*)a.q_pe + mh * a.d_rope + 2 * i;
     o[0] = y0;
     o[1] = y1;
@@ -197,12 +231,15 @@ __global__ __launch_bounds__(256) void absorb_f32_kernel(AbsorbArgs a) {
 
 hipError_t launch_absorb_bf16(const AbsorbArgs& a, bool fp8_out, hipStream_t s) {
   const int nmb = (a.batch * a.q_len + AB_M - 1) / AB_M;
-  const unsigned grid = (unsigned)(nmb * a.n_heads);
-  if (grid == 0) return hipSuccess;
-  if (fp8_out)
-    hipLaunchKernelGGL(absorb_bf16_kernel<true>, dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(absorb_bf16_kernel<false>, dim3(grid), dim3(256), 0, s, a);
+  if (nmb * a.n_heads == 0) return hipSuccess;
+  if (fp8_out) {
+    hipLaunchKernelGGL((absorb_bf16_kernel<AB_N, true>), dim3((unsigned)(nmb * a.n_heads)),
+                       dim3(256), 0, s, a);
+  } else {
+    constexpr int NB = 128;
+    hipLaunchKernelGGL((absorb_bf16_kernel<NB, false>),
+                       dim3((unsigned)(nmb * a.n_heads * (AB_N / NB))), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -16,82 +16,103 @@
 namespace mla {
 namespace {
 
-// First chunk (= partial slot) of unit (b, rg) and its chunk count.
-__device__ __forceinline__ void unit_slots(const CombineArgs& a, int64_t nt, int b, int rg,
-                                           int lane, int& first, int& count) {
-  const int before = plan_chunks_before(a.seqlens, b, a.row_groups, nt, a.num_wg, lane);
-  const int len = uni(a.seqlens[b]);
-  count = plan_splits(tiles_of(len), nt, a.num_wg);
-  first = before + rg * count;
+// First chunk (= partial slot) of unit (b, rg) and its chunk count, as the
+// decode pass recorded them (a sequence with no cached token has no chunk).
+__device__ __forceinline__ void unit_slots(const CombineArgs& a, int b, int rg, int& first,
+                                           int& count) {
+  if (a.seqlens[b] <= 0) {
+    first = 0;
+    count = 0;
+    return;
+  }
+  const int64_t u = (int64_t)b * a.row_groups + rg;
+  first = a.unit_chunks[2 * u];
+  count = a.unit_chunks[2 * u + 1];
 }
 
-// Merge the partials of one row into `dst` (d_lat floats or bf16), one wave.
-// Lane l handles latent dims [8l, 8l + 8) (d_lat <= 512, multiple of 8).
-// Returns the row's log-sum-exp.
-__device__ __forceinline__ float merge_row(const CombineArgs& a, int first, int count, int r,
-                                           int lane, float (&acc)[8]) {
+// Merge one 64-dim slice [64 sl, 64 sl + 64) of one row's partials (one
+// thread).  Partials are bf16 when the activations are bf16 and f32
+// otherwise.  Returns the row's log-sum-exp (-inf: no visible key, acc = 0).
+constexpr int SLICE = 64;
+
+__device__ __forceinline__ void load_slice(const CombineArgs& a, int64_t slot, int r, int sl,
+                                           float (&v)[SLICE]) {
+  if (a.out_dtype == DT_BF16) {
+    const uint16_t* src = (const uint16_t*)a.part_o + (slot * kRowsPerWG + r) * a.d_lat + sl * SLICE;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int c = 0; c < SLICE / 8; ++c) {
+      const u32x4 u = *(const u32x4*)(src + c * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[c * 8 + 2 * e] = __uint_as_float(u[e] << 16);
+        v[c * 8 + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+      }
+    }
+  } else {
+    const float* src = (const float*)a.part_o + (slot * kRowsPerWG + r) * a.d_lat + sl * SLICE;
+#pragma unroll
+    for (int c = 0; c < SLICE / 4; ++c) {
+      const f32x4 u = *(const f32x4*)(src + c * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[c * 4 + e] = u[e];
+    }
+  }
+}
+
+__device__ __forceinline__ float merge_slice(const CombineArgs& a, int first, int count, int r,
+                                             int sl, float (&acc)[SLICE]) {
+#pragma unroll
+  for (int e = 0; e < SLICE; ++e) acc[e] = 0.f;
   float mx = -INFINITY;
-  for (int s = 0; s < count; ++s) mx = fmaxf(mx, a.part_lse[(int64_t)(first + s) * kRowsPerWG + r]);
+  for (int s = 0; s < count; ++s)
+    mx = fmaxf(mx, a.part_lse[(int64_t)(first + s) * kRowsPerWG + r]);
   if (mx == -INFINITY) return -INFINITY;
   float tot = 0.f;
   for (int s = 0; s < count; ++s) {
-    const int64_t slot = first + s;
-    const float ls = a.part_lse[slot * kRowsPerWG + r];
+    const float ls = a.part_lse[(int64_t)(first + s) * kRowsPerWG + r];
     if (ls == -INFINITY) continue;
     const float wgt = __expf(ls - mx);
     tot += wgt;
-    if (lane * 8 < a.d_lat) {
-      const float* src = a.part_o + (slot * kRowsPerWG + r) * a.d_lat + lane * 8;
-      const f32x4 v0 = *(const f32x4*)src;
-      const f32x4 v1 = *(const f32x4*)(src + 4);
+    float v[SLICE];
+    load_slice(a, first + s, r, sl, v);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += wgt * v0[e];
-        acc[4 + e] += wgt * v1[e];
-      }
-    }
+    for (int e = 0; e < SLICE; ++e) acc[e] += wgt * v[e];
   }
   const float inv = 1.0f / tot;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] *= inv;
+  for (int e = 0; e < SLICE; ++e) acc[e] *= inv;
   return mx + __logf(tot);
 }
 
-// out = o~ (latent output): one wave per (b, j, h) row.
+// out = o~ (latent output): a workgroup merges 32 rows, thread = (row, slice).
+constexpr int ROWS_PER_WG = 32;
+
 __global__ __launch_bounds__(256) void combine_latent_kernel(CombineArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int ml = threadIdx.x / 8, sl = threadIdx.x % 8;
+  const int64_t row = (int64_t)blockIdx.x * ROWS_PER_WG + ml;
   const int64_t rows = (int64_t)a.batch * a.q_len * a.n_heads;
-  if (row >= rows) return;
+  if (row >= rows || sl * SLICE >= a.d_lat) return;
   const int b = (int)(row / ((int64_t)a.q_len * a.n_heads));
   const int jh = (int)(row % ((int64_t)a.q_len * a.n_heads));
-  const int rg = jh / kRowsPerWG, r = jh % kRowsPerWG;
-  const int64_t nt = plan_total_tiles(a.seqlens, a.batch, a.row_groups, lane);
-  float acc[8];
-  float lse = -INFINITY;
-  if (nt > 0) {
-    int first, count;
-    unit_slots(a, nt, b, rg, lane, first, count);
-    lse = merge_row(a, first, count, r, lane, acc);
-  }
-  if (lse == -INFINITY) {
+  int first, count;
+  unit_slots(a, b, jh / kRowsPerWG, first, count);
+  float acc[SLICE];
+  const float lse = merge_slice(a, first, count, jh % kRowsPerWG, sl, acc);
+  if (a.out_dtype == DT_BF16) {
+    uint16_t* o = (uint16_t*)a.out + row * a.d_lat + sl * SLICE;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int c = 0; c < SLICE / 8; ++c)
+      *(u32x4*)(o + c * 8) = u32x4{pack_bf16x2(acc[c * 8], acc[c * 8 + 1]),
+                                   pack_bf16x2(acc[c * 8 + 2], acc[c * 8 + 3]),
+                                   pack_bf16x2(acc[c * 8 + 4], acc[c * 8 + 5]),
+                                   pack_bf16x2(acc[c * 8 + 6], acc[c * 8 + 7])};
+  } else {
+    float* o = (float*)a.out + row * a.d_lat + sl * SLICE;
+#pragma unroll
+    for (int c = 0; c < SLICE / 4; ++c)
+      *(f32x4*)(o + c * 4) = f32x4{acc[c * 4], acc[c * 4 + 1], acc[c * 4 + 2], acc[c * 4 + 3]};
   }
-  if (lane * 8 < a.d_lat) {
-    if (a.out_dtype == DT_BF16) {
-      uint16_t* o = (uint16_t*)a.out + row * a.d_lat + lane * 8;
-      *(u32x4*)o = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-    } else {
-      float* o = (float*)a.out + row * a.d_lat + lane * 8;
-      *(f32x4*)o = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      *(f32x4*)(o + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
-    }
-  }
-  if (a.lse != nullptr && lane == 0) a.lse[row] = lse;
+  if (a.lse != nullptr && sl == 0) a.lse[row] = lse;
 }
 
 // bf16: out[m, h, :] = W_UV[h] o~[m, h, :] for a block of 32 rows m = (b, j)
@@ -113,29 +134,29 @@ __global__ __launch_bounds__(256) void combine_uv_bf16_kernel(CombineArgs a) {
   const int h = blk / nmb;
   const int mb = blk % nmb;
   const int m_total = a.batch * a.q_len;
-  const int64_t nt = plan_total_tiles(a.seqlens, a.batch, a.row_groups, lane);
 
-  // 1. merge the block's rows (8 per wave) into LDS
-  for (int i = 0; i < UV_M / 4; ++i) {
-    const int ml = w * (UV_M / 4) + i;
+  // 1. merge the block's rows into LDS: thread = (row, 64-dim slice)
+  {
+    const int ml = threadIdx.x / 8, sl = threadIdx.x % 8;
     const int m = mb * UV_M + ml;
-    float acc[8];
+    float acc[SLICE];
     float lse = -INFINITY;
-    if (m < m_total && nt > 0) {
+    if (m < m_total) {
       const int b = m / a.q_len, j = m % a.q_len;
       const int jh = j * a.n_heads + h;
       int first, count;
-      unit_slots(a, nt, b, jh / kRowsPerWG, lane, first, count);
-      lse = merge_row(a, first, count, jh % kRowsPerWG, lane, acc);
-    }
-    if (lse == -INFINITY) {
+      unit_slots(a, b, jh / kRowsPerWG, first, count);
+      lse = merge_slice(a, first, count, jh % kRowsPerWG, sl, acc);
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      for (int e = 0; e < SLICE; ++e) acc[e] = 0.f;
     }
-    *(u32x4*)&s_o[ml][lane * 8] = u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-    if (a.lse != nullptr && lane == 0 && m < m_total)
-      a.lse[(int64_t)m * a.n_heads + h] = lse;
+#pragma unroll
+    for (int c = 0; c < SLICE / 8; ++c)
+      *(u32x4*)&s_o[ml][sl * SLICE + c * 8] =
+          u32x4{pack_bf16x2(acc[c * 8], acc[c * 8 + 1]), pack_bf16x2(acc[c * 8 + 2], acc[c * 8 + 3]),
+                pack_bf16x2(acc[c * 8 + 4], acc[c * 8 + 5]), pack_bf16x2(acc[c * 8 + 6], acc[c * 8 + 7])};
+    if (a.lse != nullptr && sl == 0 && m < m_total) a.lse[(int64_t)m * a.n_heads + h] = lse;
   }
   __syncthreads();
 
@@ -178,35 +199,30 @@ __global__ __launch_bounds__(256) void combine_uv_bf16_kernel(CombineArgs a) {
 // merged rows in LDS, plain fp32 FMAs.
 __global__ __launch_bounds__(256) void combine_uv_f32_kernel(CombineArgs a) {
   __shared__ float s_o[UV_M][UV_DLAT + 4];
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
   const int nmb = (a.batch * a.q_len + UV_M - 1) / UV_M;
   const int h = blockIdx.x / nmb;
   const int mb = blockIdx.x % nmb;
   const int m_total = a.batch * a.q_len;
-  const int64_t nt = plan_total_tiles(a.seqlens, a.batch, a.row_groups, lane);
-  for (int i = 0; i < UV_M / 4; ++i) {
-    const int ml = w * (UV_M / 4) + i;
+  {
+    const int ml = threadIdx.x / 8, sl = threadIdx.x % 8;
     const int m = mb * UV_M + ml;
-    float acc[8];
-    float lse = -INFINITY;
-    if (m < m_total && nt > 0) {
-      const int b = m / a.q_len, j = m % a.q_len;
-      const int jh = j * a.n_heads + h;
-      int first, count;
-      unit_slots(a, nt, b, jh / kRowsPerWG, lane, first, count);
-      lse = merge_row(a, first, count, jh % kRowsPerWG, lane, acc);
-    }
-    if (lse == -INFINITY) {
+    if (sl * SLICE < a.d_lat) {
+      float acc[SLICE];
+      float lse = -INFINITY;
+      if (m < m_total) {
+        const int b = m / a.q_len, j = m % a.q_len;
+        const int jh = j * a.n_heads + h;
+        int first, count;
+        unit_slots(a, b, jh / kRowsPerWG, first, count);
+        lse = merge_slice(a, first, count, jh % kRowsPerWG, sl, acc);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    }
-    if (lane * 8 < a.d_lat) {
+        for (int e = 0; e < SLICE; ++e) acc[e] = 0.f;
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) s_o[ml][lane * 8 + e] = acc[e];
+      for (int e = 0; e < SLICE; ++e) s_o[ml][sl * SLICE + e] = acc[e];
+      if (a.lse != nullptr && sl == 0 && m < m_total) a.lse[(int64_t)m * a.n_heads + h] = lse;
     }
-    if (a.lse != nullptr && lane == 0 && m < m_total)
-      a.lse[(int64_t)m * a.n_heads + h] = lse;
   }
   __syncthreads();
   const float* W = (const float*)a.w_uv + (int64_t)h * a.d_v * a.d_lat;
@@ -226,7 +242,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.q_len * a.n_heads;
   if (rows == 0) return hipSuccess;
   if (a.w_uv == nullptr) {
-    hipLaunchKernelGGL(combine_latent_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(combine_latent_kernel, dim3((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)),
+                       dim3(256), 0, s, a);
   } else {
     const int nmb = (a.batch * a.q_len + UV_M - 1) / UV_M;
     const unsigned grid = (unsigned)(nmb * a.n_heads);

@@ -37,8 +37,12 @@
 //     references and runs its chunk once more from a private LDS stage.  The
 //     accumulator is thus only ever written by MFMAs, which keeps it resident
 //     in AGPRs.
-//   * LDS rows are XOR-swizzled on 16-byte chunks (chunk c of token t is
-//     stored at c ^ (t & 7)) so both read patterns spread over the banks.
+//   * LDS rows are XOR-swizzled on 16-byte chunks so both read patterns are
+//     bank-conflict free: latent chunk c of token t sits at c ^ lat_key(t),
+//     where lat_key gives the 16 tokens of a QK read 16 different keys and
+//     the 4 tokens of a transpose-read group keys that differ above bit 0
+//     (so a chunk pair 2d, 2d+1 of one token never shares banks with
+//     another's); rotary chunk c sits at c ^ rope_key(t).
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -61,6 +65,10 @@ constexpr float kRefSlack = 64.0f;         // log2 units
 
 __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NSTAGE * STAGE];
 
+// swizzle keys (see the header); both depend on t & 15 only
+__device__ __forceinline__ int lat_key(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
+__device__ __forceinline__ int rope_key(int t) { return (t >> 1) & 7; }
+
 __device__ __forceinline__ MLA_LDS uint8_t* stage_base(int st) {
   return (MLA_LDS uint8_t*)s_ring + st * STAGE;
 }
@@ -82,12 +90,12 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, int b, int len, 
   for (int q = 0; q < 8; ++q) {
     const int t = w * 8 + q;
     const int tc = min(tok0 + t, last) - tok0;
-    dma16(lat + tc * LAT_ROW + (uint32_t)((lane ^ q) << 4), dst + t * LAT_ROW);
+    dma16(lat + tc * LAT_ROW + (uint32_t)((lane ^ lat_key(t)) << 4), dst + t * LAT_ROW);
   }
   {
     const int t = w * 8 + (lane >> 3);
     const int tc = min(tok0 + t, last) - tok0;
-    const uint32_t off = (uint32_t)(tc * ROPE_ROW + (((lane & 7) ^ (lane >> 3)) << 4));
+    const uint32_t off = (uint32_t)(tc * ROPE_ROW + (((lane & 7) ^ rope_key(t)) << 4));
     dma16(rope + off, dst + LAT_STAGE + w * 8 * ROPE_ROW);
   }
 }
@@ -109,7 +117,8 @@ struct SegState {
   bool redo;            // a score passed m_ref + 64 with mass already accumulated
 };
 
-// The chunk's partial: o~ / l and its natural-log log-sum-exp.
+// The chunk's partial: o~ / l (rounded to bf16, like the output it feeds)
+// and its natural-log log-sum-exp.
 __device__ __forceinline__ void write_partial(const DecodeArgs& a, SegState& S, int64_t slot,
                                               int w, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
@@ -121,9 +130,12 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, SegState& S, 
     const float lse = lsum > 0.f ? (S.m[hb] + __log2f(lsum)) * kLn2 : -INFINITY;
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
     const int row = w * 32 + hb * 16 + lr;
-    float* dst = a.part_o + (slot * kRowsPerWG + row) * D_LAT + lg * 4;
+    uint16_t* dst = (uint16_t*)a.part_o + (slot * kRowsPerWG + row) * D_LAT + lg * 4;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) *(f32x4*)(dst + db * 16) = S.o[hb][db] * inv;
+    for (int db = 0; db < DB; ++db) {
+      const f32x4 v = S.o[hb][db] * inv;
+      *(u32x2*)(dst + db * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    }
     if (lg == 0) a.part_lse[slot * kRowsPerWG + row] = lse;
   }
 }
@@ -140,28 +152,36 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) sacc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int f = lr & 7;                         // swizzle key of rows lr and 16 + lr
-  const int pe = (lg ^ f) << 4;                 // chunk position for even k-steps
-  const int po = ((4 + lg) ^ f) << 4;           // ... odd k-steps
-  const MLA_LDS uint8_t* lat_e = lat + lr * LAT_ROW + pe;
-  const MLA_LDS uint8_t* lat_o = lat + lr * LAT_ROW + po;
-  const MLA_LDS uint8_t* rope_e = rope + lr * ROPE_ROW + pe;
-  const MLA_LDS uint8_t* rope_o = rope + lr * ROPE_ROW + po;
+  // latent chunk kk*4 + lg of token tb*16 + lr sits at ((kk & 3)*4 + lg) ^ key
+  // within the 16-chunk group kk >> 2 (key < 16); rotary chunk k2*4 + lg at
+  // (k2*4 + lg) ^ rope_key
+  const int fk = lat_key(lr);
+  const int gk = rope_key(lr);
+  const MLA_LDS uint8_t* lat_q[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) lat_q[v] = lat + lr * LAT_ROW + (((v * 4 + lg) ^ fk) << 4);
+  const MLA_LDS uint8_t* rope_q[2];
+#pragma unroll
+  for (int v = 0; v < 2; ++v) rope_q[v] = rope + lr * ROPE_ROW + (((v * 4 + lg) ^ gk) << 4);
   auto load_k = [&](int kk, int tb) -> u16x8 {
     if (kk < KS_LAT)
-      return *(const MLA_LDS u16x8*)(((kk & 1) ? lat_o : lat_e) + tb * 16 * LAT_ROW +
-                                     (kk >> 1) * 128);
-    const int k2 = kk - KS_LAT;
-    return *(const MLA_LDS u16x8*)(((k2 & 1) ? rope_o : rope_e) + tb * 16 * ROPE_ROW +
-                                   (k2 >> 1) * 128);
+      return *(const MLA_LDS u16x8*)(lat_q[kk & 3] + tb * 16 * LAT_ROW + (kk >> 2) * 256);
+    return *(const MLA_LDS u16x8*)(rope_q[kk - KS_LAT] + tb * 16 * ROPE_ROW);
   };
-  u16x8 nxt0 = load_k(0, 0), nxt1 = load_k(0, 1);
+  // A operands are read QK_AHEAD k-steps ahead of their MFMAs
+  constexpr int QK_AHEAD = 3;
+  u16x8 ka[QK_AHEAD][2];
+#pragma unroll
+  for (int j = 0; j < QK_AHEAD; ++j) {
+    ka[j][0] = load_k(j, 0);
+    ka[j][1] = load_k(j, 1);
+  }
 #pragma unroll
   for (int kk = 0; kk < KS; ++kk) {
-    const u16x8 cur0 = nxt0, cur1 = nxt1;
-    if (kk + 1 < KS) {
-      nxt0 = load_k(kk + 1, 0);
-      nxt1 = load_k(kk + 1, 1);
+    const u16x8 cur0 = ka[kk % QK_AHEAD][0], cur1 = ka[kk % QK_AHEAD][1];
+    if (kk + QK_AHEAD < KS) {
+      ka[kk % QK_AHEAD][0] = load_k(kk + QK_AHEAD, 0);
+      ka[kk % QK_AHEAD][1] = load_k(kk + QK_AHEAD, 1);
     }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
@@ -223,8 +243,8 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
 #pragma unroll
       for (int r = 0; r < 4; r += 2) {
         // (the clamp only matters in a pass that will be redone)
-        const float p0 = (mref == -INFINITY) ? 0.f : exp2f(fminf(sv[hb][tb][r] - mref, kRefSlack));
-        const float p1 = (mref == -INFINITY) ? 0.f : exp2f(fminf(sv[hb][tb][r + 1] - mref, kRefSlack));
+        const float p0 = (mref == -INFINITY) ? 0.f : fast_exp2(fminf(sv[hb][tb][r] - mref, kRefSlack));
+        const float p1 = (mref == -INFINITY) ? 0.f : fast_exp2(fminf(sv[hb][tb][r + 1] - mref, kRefSlack));
         const uint32_t u = pack_bf16x2(p0, p1);
         pk[tb * 2 + r / 2] = u;
         psum += __uint_as_float(u << 16) + __uint_as_float(u & 0xffff0000u);
@@ -237,25 +257,28 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
   // transpose read: lane (lg, lr) addresses token row lg*4 + lr/4 (and +16),
   // latent dims db*16 + (lr&3)*4 .. +3, i.e. chunk 2db + (lr&3)/2
   const int t1 = lg * 4 + (lr >> 2);
-  const int f1 = t1 & 7;
+  const int f1 = lat_key(t1);
   const int cbit = (lr & 3) >> 1;
   const int half = (lr & 1) << 3;
-  const MLA_LDS uint8_t* pv_base[4];
+  // chunk 2db + cbit sits at ((2(db & 7) + cbit) ^ f1) in group db >> 3
+  const MLA_LDS uint8_t* pv_base[8];
 #pragma unroll
-  for (int v = 0; v < 4; ++v)
+  for (int v = 0; v < 8; ++v)
     pv_base[v] = lat + t1 * LAT_ROW + (((2 * v + cbit) ^ f1) << 4) + half;
   auto load_c = [&](int db) -> u16x8 {
-    const MLA_LDS uint8_t* p = pv_base[db & 3] + (db >> 2) * 128;
+    const MLA_LDS uint8_t* p = pv_base[db & 7] + (db >> 3) * 256;
     const u16x4 lo = lds_read_tr16(p);
     const u16x4 hi = lds_read_tr16(p + 16 * LAT_ROW);
     return u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   };
-  u16x8 c0 = load_c(0), c1 = load_c(1);
+  constexpr int PV_AHEAD = 4;
+  u16x8 ca[PV_AHEAD];
+#pragma unroll
+  for (int j = 0; j < PV_AHEAD; ++j) ca[j] = load_c(j);
 #pragma unroll
   for (int db = 0; db < DB; ++db) {
-    const u16x8 av = c0;
-    c0 = c1;
-    if (db + 2 < DB) c1 = load_c(db + 2);
+    const u16x8 av = ca[db % PV_AHEAD];
+    if (db + PV_AHEAD < DB) ca[db % PV_AHEAD] = load_c(db + PV_AHEAD);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) S.o[hb][db] = mfma_bf16_16x16x32(av, pf[hb], S.o[hb][db]);
     __builtin_amdgcn_sched_barrier(0);
@@ -272,6 +295,12 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
   if (nt == 0) return;
   Chunk ch;
   if (!plan_find_chunk(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, g, lane, ch)) return;
+  if (ch.c == 0 && threadIdx.x == 0) {
+    // where the combine pass finds this unit's partials
+    const int64_t u = (int64_t)ch.b * a.row_groups + ch.rg;
+    a.unit_chunks[2 * u] = g;
+    a.unit_chunks[2 * u + 1] = ch.splits;
+  }
   const int k0 = (int)((int64_t)ch.c * ch.tiles / ch.splits);
   const int k1 = (int)((int64_t)(ch.c + 1) * ch.tiles / ch.splits);
   const int n = k1 - k0;

@@ -24,6 +24,12 @@ __global__ __launch_bounds__(128) void decode_f32_kernel(DecodeArgs a) {
   if (nt == 0) return;
   Chunk ch;
   if (!plan_find_chunk(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, g, lane, ch)) return;
+  if (ch.c == 0 && threadIdx.x == 0) {
+    // where the combine pass finds this unit's partials
+    const int64_t u = (int64_t)ch.b * a.row_groups + ch.rg;
+    a.unit_chunks[2 * u] = g;
+    a.unit_chunks[2 * u + 1] = ch.splits;
+  }
   const int k0 = (int)((int64_t)ch.c * ch.tiles / ch.splits);
   const int k1 = (int)((int64_t)(ch.c + 1) * ch.tiles / ch.splits);
   const int t_begin = k0 * kTile;
@@ -76,7 +82,7 @@ __global__ __launch_bounds__(128) void decode_f32_kernel(DecodeArgs a) {
   }
   const int64_t slot = g;
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  float* dst = a.part_o + (slot * kRowsPerWG + row) * a.d_lat;
+  float* dst = (float*)a.part_o + (slot * kRowsPerWG + row) * a.d_lat;
 #pragma unroll
   for (int d = 0; d < DL_MAX; ++d)
     if (d < a.d_lat) dst[d] = o[d] * inv;

@@ -138,6 +138,10 @@ __device__ inline bool plan_find_chunk(const int32_t* seqlens, int batch, int ro
   return false;
 }
 
+// 2^x with the hardware v_exp_f32 (results below 2^-126 flush to 0, which
+// only drops probabilities that small relative to the row's reference)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
   f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));

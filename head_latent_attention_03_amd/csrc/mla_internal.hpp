@@ -29,9 +29,9 @@ struct DecodeArgs {
   const void* kv_rope;
   const int32_t* block_table;
   const int32_t* seqlens;
-  float* part_o;             // [slots, 128, d_lat] f32
+  void* part_o;              // [slots, 128, d_lat] bf16 (bf16 activations) or f32
   float* part_lse;           // [slots, 128]        f32 (natural log)
-  float* part_tmp;           // [slots, 128, d_lat] f32 scratch for mid-chunk merges
+  int32_t* unit_chunks;      // [units, 2]: first chunk and chunk count of each unit
   int32_t max_pages, batch, q_len, n_heads, causal;
   int32_t d_lat, d_rope;
   int32_t num_wg, row_groups;
@@ -39,8 +39,9 @@ struct DecodeArgs {
 };
 
 struct CombineArgs {
-  const float* part_o;
+  const void* part_o;        // bf16 when out_dtype is bf16, else f32
   const float* part_lse;
+  const int32_t* unit_chunks;  // [units, 2] as written by the decode pass
   const int32_t* seqlens;
   const void* w_uv;          // may be null
   void* out;
