@@ -46,6 +46,11 @@
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
+// 16-row MFMA blocks per wave: 1 (8 waves, two per SIMD) or 2 (4 waves)
+#ifndef MLA_DECODE_HB
+#define MLA_DECODE_HB 1
+#endif
+
 namespace mla {
 namespace {
 
@@ -63,7 +68,17 @@ constexpr int STAGE = LAT_STAGE + ROPE_STAGE;
 constexpr int NSTAGE = 4;
 constexpr float kRefSlack = 64.0f;         // log2 units
 
+// Wave geometry: HB 16-row MFMA blocks per wave, 128 / (16 HB) waves.
+template <int HB>
+struct Geo {
+  static constexpr int kWavesWG = kRowsPerWG / (16 * HB);
+  static constexpr int kThreads = 64 * kWavesWG;
+  static constexpr int kLatRows = kTile / kWavesWG;  // latent rows each wave copies per tile
+  static constexpr int kDma = kLatRows + 1;          // copies per wave per tile
+};
+
 __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NSTAGE * STAGE];
+__shared__ int s_redo;
 
 // swizzle keys (see the header); both depend on t & 15 only
 __device__ __forceinline__ int lat_key(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
@@ -73,11 +88,15 @@ __device__ __forceinline__ MLA_LDS uint8_t* stage_base(int st) {
   return (MLA_LDS uint8_t*)s_ring + st * STAGE;
 }
 
-// Issue the 9 DMA instructions of this wave for tile k of sequence b into
-// stage st.  Tokens past the end of the sequence re-read its last token
-// (finite data that the mask then ignores), so every wave issues the same count.
+// Issue this wave's DMA instructions for tile k of sequence b into stage st:
+// kLatRows latent rows, and the rotary rows of the same tokens (one copy, on
+// fewer lanes when a wave's rotary rows fill less than 1 KiB).  Tokens past
+// the end of the sequence re-read its last token (finite data that the mask
+// then ignores), so every wave issues the same count.
+template <int HB>
 __device__ __forceinline__ void issue_tile(const DecodeArgs& a, int b, int len, int k, int st,
                                            int w, int lane) {
+  constexpr int NL = Geo<HB>::kLatRows;
   const int tok0 = k * kTile;
   const int last = len - 1;
   const int page = sload_i32(a.block_table + (int64_t)b * a.max_pages, tok0 / kPage);
@@ -86,50 +105,65 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, int b, int len, 
   const uint8_t* lat = (const uint8_t*)a.kv_lat + row0 * LAT_ROW;
   const uint8_t* rope = (const uint8_t*)a.kv_rope + row0 * ROPE_ROW;
   MLA_LDS uint8_t* dst = stage_base(st);
+  // lat_key(w*NL + q) = lat_key(w*NL) ^ 2q for q < NL, so the source chunk
+  // offsets of the wave's rows are one per-lane value XOR 32q (kept opaque so
+  // the compiler does not hold all of them in registers across the loop)
+  uint32_t off0 = (uint32_t)((lane ^ lat_key(w * NL)) << 4);
+  asm volatile("" : "+v"(off0));
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int t = w * 8 + q;
+  for (int q = 0; q < NL; ++q) {
+    const int t = w * NL + q;
     const int tc = min(tok0 + t, last) - tok0;
-    dma16(lat + tc * LAT_ROW + (uint32_t)((lane ^ lat_key(t)) << 4), dst + t * LAT_ROW);
+    dma16(lat + tc * LAT_ROW + (off0 ^ (uint32_t)(q << 5)), dst + t * LAT_ROW);
   }
   {
-    const int t = w * 8 + (lane >> 3);
+    const int t = w * NL + (lane >> 3);
     const int tc = min(tok0 + t, last) - tok0;
     const uint32_t off = (uint32_t)(tc * ROPE_ROW + (((lane & 7) ^ rope_key(t)) << 4));
-    dma16(rope + off, dst + LAT_STAGE + w * 8 * ROPE_ROW);
+    if (NL * ROPE_ROW >= 1024 || lane < NL * 8)
+      dma16(rope + off, dst + LAT_STAGE + w * NL * ROPE_ROW);
   }
 }
 
-__device__ __forceinline__ void wait_tiles(int remaining_after) {
-  // this wave's DMA for the current tile is done once at most
-  // 9 * min(2, remaining_after) of its newer VMEM ops are outstanding
-  if (remaining_after >= 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-  else if (remaining_after == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// This wave's copies for the current tile are done once at most
+// kDma * min(2, remaining_after) of its newer VMEM ops are outstanding.
+template <int HB>
+__device__ __forceinline__ void wait_tiles(int remaining_after) {
+  constexpr int D = Geo<HB>::kDma;
+  if (remaining_after >= 2) wait_vm<2 * D>();
+  else if (remaining_after == 1) wait_vm<D>();
+  else wait_vm<0>();
+}
+
+template <int HB>
 struct SegState {
-  u16x8 q[2][KS];       // absorbed query (B operand), per 16-row block
-  f32x4 o[2][DB];       // O^T accumulator: lane holds head lr, 4 latent dims
-  float m[2], l[2];     // reference max (log2 units, scaled) and per-lane sum
-  int lim[2];           // keys visible to the lane's row: t < lim
-  float tmax[2];        // largest score this lane has seen (log2 units, scaled)
+  u16x8 q[HB][KS];      // absorbed query (B operand), per 16-row block
+  f32x4 o[HB][DB];      // O^T accumulator: lane holds head lr, 4 latent dims
+  float m[HB], l[HB];   // reference max (log2 units, scaled) and per-lane sum
+  int lim[HB];          // keys visible to the lane's row: t < lim
+  float tmax[HB];       // largest score this lane has seen (log2 units, scaled)
   bool redo;            // a score passed m_ref + 64 with mass already accumulated
 };
 
 // The chunk's partial: o~ / l (rounded to bf16, like the output it feeds)
 // and its natural-log log-sum-exp.
-__device__ __forceinline__ void write_partial(const DecodeArgs& a, SegState& S, int64_t slot,
-                                              int w, int lane) {
+template <int HB>
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, SegState<HB>& S,
+                                              int64_t slot, int w, int lane) {
   const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
+  for (int hb = 0; hb < HB; ++hb) {
     float lsum = S.l[hb];
     lsum = wave_sum_xor(lsum, 16);
     lsum = wave_sum_xor(lsum, 32);
     const float lse = lsum > 0.f ? (S.m[hb] + __log2f(lsum)) * kLn2 : -INFINITY;
     const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-    const int row = w * 32 + hb * 16 + lr;
+    const int row = w * 16 * HB + hb * 16 + lr;
     uint16_t* dst = (uint16_t*)a.part_o + (slot * kRowsPerWG + row) * D_LAT + lg * 4;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
@@ -140,36 +174,52 @@ __device__ __forceinline__ void write_partial(const DecodeArgs& a, SegState& S, 
   }
 }
 
-__device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, int st, int tok0,
-                                             int lane) {
+// Per-lane LDS byte offsets (from a stage's base) of the three read patterns.
+// Every address the tile reads is one of them XOR a small constant:
+//   QK latent, chunk group v:  qk ^ (v << 6)   ((v*4 + lg) ^ key = (lg ^ key) ^ 4v)
+//   QK rotary, chunk group v:  rp ^ (v << 6)
+//   PV transpose, column db:   pv ^ ((db & 7) << 5), + 256 per 8 columns
+// (the stage base is 1 KiB aligned and the XORed bits never carry).
+struct LaneOff {
+  uint32_t qk, rp, pv;
+};
+
+__device__ __forceinline__ LaneOff lane_offsets(int lane) {
   const int lr = lane & 15, lg = lane >> 4;
+  const int t1 = lg * 4 + (lr >> 2);
+  LaneOff o;
+  o.qk = (uint32_t)(lr * LAT_ROW + ((lg ^ lat_key(lr)) << 4));
+  o.rp = (uint32_t)(LAT_STAGE + lr * ROPE_ROW + ((lg ^ rope_key(lr)) << 4));
+  o.pv = (uint32_t)(t1 * LAT_ROW + ((((lr & 3) >> 1) ^ lat_key(t1)) << 4) + ((lr & 1) << 3));
+  return o;
+}
+
+template <int HB>
+__device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState<HB>& S, int st,
+                                             int tok0, int lane, LaneOff lo) {
+  const int lg = lane >> 4;
   const MLA_LDS uint8_t* lat = stage_base(st);
-  const MLA_LDS uint8_t* rope = lat + LAT_STAGE;
+  // opaque per tile, so the XOR variants are formed where they are used
+  asm volatile("" : "+v"(lo.qk), "+v"(lo.rp), "+v"(lo.pv));
 
   // ---- S^T[t, h] = K[t, :] . Q[h, :]
-  f32x4 sacc[2][2];
+  f32x4 sacc[2][HB];
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) sacc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hb = 0; hb < HB; ++hb) sacc[tb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // latent chunk kk*4 + lg of token tb*16 + lr sits at ((kk & 3)*4 + lg) ^ key
   // within the 16-chunk group kk >> 2 (key < 16); rotary chunk k2*4 + lg at
   // (k2*4 + lg) ^ rope_key
-  const int fk = lat_key(lr);
-  const int gk = rope_key(lr);
-  const MLA_LDS uint8_t* lat_q[4];
-#pragma unroll
-  for (int v = 0; v < 4; ++v) lat_q[v] = lat + lr * LAT_ROW + (((v * 4 + lg) ^ fk) << 4);
-  const MLA_LDS uint8_t* rope_q[2];
-#pragma unroll
-  for (int v = 0; v < 2; ++v) rope_q[v] = rope + lr * ROPE_ROW + (((v * 4 + lg) ^ gk) << 4);
   auto load_k = [&](int kk, int tb) -> u16x8 {
     if (kk < KS_LAT)
-      return *(const MLA_LDS u16x8*)(lat_q[kk & 3] + tb * 16 * LAT_ROW + (kk >> 2) * 256);
-    return *(const MLA_LDS u16x8*)(rope_q[kk - KS_LAT] + tb * 16 * ROPE_ROW);
+      return *(const MLA_LDS u16x8*)(lat + (lo.qk ^ (uint32_t)((kk & 3) << 6)) + tb * 16 * LAT_ROW +
+                                     (kk >> 2) * 256);
+    return *(const MLA_LDS u16x8*)(lat + (lo.rp ^ (uint32_t)((kk - KS_LAT) << 6)) +
+                                   tb * 16 * ROPE_ROW);
   };
   // A operands are read QK_AHEAD k-steps ahead of their MFMAs
-  constexpr int QK_AHEAD = 3;
+  constexpr int QK_AHEAD = HB == 1 ? 2 : 3;
   u16x8 ka[QK_AHEAD][2];
 #pragma unroll
   for (int j = 0; j < QK_AHEAD; ++j) {
@@ -184,7 +234,7 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
       ka[kk % QK_AHEAD][1] = load_k(kk + QK_AHEAD, 1);
     }
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < HB; ++hb) {
       sacc[0][hb] = mfma_bf16_16x16x32(cur0, S.q[hb][kk], sacc[0][hb]);
       sacc[1][hb] = mfma_bf16_16x16x32(cur1, S.q[hb][kk], sacc[1][hb]);
     }
@@ -195,12 +245,13 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
   // Common path: every score is below its row's reference + 64, so the
   // probabilities follow with no cross-lane traffic.  Otherwise (the row's
   // first scores, or a jump) the row maximum is formed across the row's four
-  // lanes and the reference moves, banking what was accumulated if needed.
-  float sv[2][2][4];
-  float lmax[2];
+  // lanes: a row's first scores set its reference, a later jump marks the
+  // wave for a second pass with the true maxima.
+  float sv[HB][2][4];
+  float lmax[HB];
   bool need_lane = false;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
+  for (int hb = 0; hb < HB; ++hb) {
     float mx = -INFINITY;
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
@@ -216,10 +267,8 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
     need_lane |= mx > S.m[hb] + kRefSlack;
   }
   if (__ballot(need_lane)) {
-    // a row's first scores set its reference; a later jump marks the wave
-    // for a second pass with the true maxima
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+    for (int hb = 0; hb < HB; ++hb) {
       float mx = lmax[hb];
       mx = wave_max_xor(mx, 16);
       mx = wave_max_xor(mx, 32);
@@ -232,9 +281,9 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
     }
     S.redo = __ballot(S.redo) != 0;
   }
-  u16x8 pf[2];
+  u16x8 pf[HB];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
+  for (int hb = 0; hb < HB; ++hb) {
     const float mref = S.m[hb];
     uint32_t pk[4];
     float psum = 0.f;
@@ -255,23 +304,15 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
 
   // ---- O^T[d, h] += C^T[d, t] P^T[t, h]
   // transpose read: lane (lg, lr) addresses token row lg*4 + lr/4 (and +16),
-  // latent dims db*16 + (lr&3)*4 .. +3, i.e. chunk 2db + (lr&3)/2
-  const int t1 = lg * 4 + (lr >> 2);
-  const int f1 = lat_key(t1);
-  const int cbit = (lr & 3) >> 1;
-  const int half = (lr & 1) << 3;
-  // chunk 2db + cbit sits at ((2(db & 7) + cbit) ^ f1) in group db >> 3
-  const MLA_LDS uint8_t* pv_base[8];
-#pragma unroll
-  for (int v = 0; v < 8; ++v)
-    pv_base[v] = lat + t1 * LAT_ROW + (((2 * v + cbit) ^ f1) << 4) + half;
+  // latent dims db*16 + (lr&3)*4 .. +3, i.e. chunk 2db + (lr&3)/2, which sits
+  // at ((2(db & 7) + (lr&3)/2) ^ key) in chunk group db >> 3
   auto load_c = [&](int db) -> u16x8 {
-    const MLA_LDS uint8_t* p = pv_base[db & 7] + (db >> 3) * 256;
-    const u16x4 lo = lds_read_tr16(p);
-    const u16x4 hi = lds_read_tr16(p + 16 * LAT_ROW);
-    return u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const MLA_LDS uint8_t* p = lat + (lo.pv ^ (uint32_t)((db & 7) << 5)) + (db >> 3) * 256;
+    const u16x4 lo4 = lds_read_tr16(p);
+    const u16x4 hi4 = lds_read_tr16(p + 16 * LAT_ROW);
+    return u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
   };
-  constexpr int PV_AHEAD = 4;
+  constexpr int PV_AHEAD = HB == 1 ? 2 : 4;
   u16x8 ca[PV_AHEAD];
 #pragma unroll
   for (int j = 0; j < PV_AHEAD; ++j) ca[j] = load_c(j);
@@ -280,19 +321,44 @@ __device__ __forceinline__ void compute_tile(const DecodeArgs& a, SegState& S, i
     const u16x8 av = ca[db % PV_AHEAD];
     if (db + PV_AHEAD < DB) ca[db % PV_AHEAD] = load_c(db + PV_AHEAD);
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) S.o[hb][db] = mfma_bf16_16x16x32(av, pf[hb], S.o[hb][db]);
+    for (int hb = 0; hb < HB; ++hb) S.o[hb][db] = mfma_bf16_16x16x32(av, pf[hb], S.o[hb][db]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-__global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
+// One pass over the chunk's tiles [k0, k0 + n): HBM -> LDS ring of 4 stages
+// with three tiles in flight, one barrier per tile.  Waves with active ==
+// false only copy their share and keep the barriers.
+template <int HB>
+__device__ __forceinline__ void run_pass(const DecodeArgs& a, SegState<HB>& S, const Chunk& ch,
+                                         int k0, int n, int w, int lane, bool active) {
+  const LaneOff lo = lane_offsets(lane);
+  issue_tile<HB>(a, ch.b, ch.len, k0, 0, w, lane);
+  if (n > 1) issue_tile<HB>(a, ch.b, ch.len, k0 + 1, 1, w, lane);
+  if (n > 2) issue_tile<HB>(a, ch.b, ch.len, k0 + 2, 2, w, lane);
+  for (int i = 0; i < n; ++i) {
+    wait_tiles<HB>(n - 1 - i);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (i + 3 < n) issue_tile<HB>(a, ch.b, ch.len, k0 + i + 3, (i + 3) & 3, w, lane);
+    if (active) compute_tile<HB>(a, S, i & 3, (k0 + i) * kTile, lane, lo);
+  }
+  // every wave is done with the ring once all have passed this barrier
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int HB>
+__global__ __launch_bounds__(Geo<HB>::kThreads, 1) void decode_bf16_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = uni(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
-  const int g = xcd_logical_id(blockIdx.x, gridDim.x);
 
   const int64_t nt = plan_total_tiles(a.seqlens, a.batch, a.row_groups, lane);
   if (nt == 0) return;
+  const int g = plan_chunk_of_block(
+      blockIdx.x, plan_chunks_before(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, lane));
+  if (g < 0) return;
   Chunk ch;
   if (!plan_find_chunk(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, g, lane, ch)) return;
   if (ch.c == 0 && threadIdx.x == 0) {
@@ -301,20 +367,21 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     a.unit_chunks[2 * u] = g;
     a.unit_chunks[2 * u + 1] = ch.splits;
   }
+  if (threadIdx.x == 0) s_redo = 0;
   const int k0 = (int)((int64_t)ch.c * ch.tiles / ch.splits);
   const int k1 = (int)((int64_t)(ch.c + 1) * ch.tiles / ch.splits);
   const int n = k1 - k0;
   const int64_t slot = g;
 
   // query rows of this unit; the (query, head) row of lane (lg, lr) in 16-row
-  // block hb is R = rg*128 + 32w + 16hb + lr
+  // block hb is R = rg*128 + 16*HB*w + 16hb + lr
   const int rows_total = a.q_len * a.n_heads;
   const uint16_t* qlat = (const uint16_t*)a.q_lat;
   const uint16_t* qpe = (const uint16_t*)a.q_pe;
-  SegState S;
+  SegState<HB> S;
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const int R = ch.rg * kRowsPerWG + w * 32 + hb * 16 + lr;
+  for (int hb = 0; hb < HB; ++hb) {
+    const int R = ch.rg * kRowsPerWG + w * 16 * HB + hb * 16 + lr;
     const bool valid = R < rows_total;
     const int j = valid ? R / a.n_heads : 0;
     const int h = valid ? R % a.n_heads : 0;
@@ -333,54 +400,44 @@ __global__ __launch_bounds__(256, 1) void decode_bf16_kernel(DecodeArgs a) {
     S.m[hb] = -INFINITY;
     S.l[hb] = 0.f;
     S.lim[hb] = valid ? (a.causal ? ch.len - a.q_len + j + 1 : ch.len) : 0;
+    S.tmax[hb] = -INFINITY;
   }
   S.redo = false;
-  S.tmax[0] = S.tmax[1] = -INFINITY;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 
-  // prologue: three tiles in flight (issued after the query loads, so the
-  // first wait below covers both)
-  issue_tile(a, ch.b, ch.len, k0, 0, w, lane);
-  if (n > 1) issue_tile(a, ch.b, ch.len, k0 + 1, 1, w, lane);
-  if (n > 2) issue_tile(a, ch.b, ch.len, k0 + 2, 2, w, lane);
+  run_pass<HB>(a, S, ch, k0, n, w, lane, true);
 
-  for (int i = 0; i < n; ++i) {
-    wait_tiles(n - 1 - i);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (i + 3 < n) issue_tile(a, ch.b, ch.len, k0 + i + 3, (i + 3) & 3, w, lane);
-    compute_tile(a, S, i & 3, (k0 + i) * kTile, lane);
-  }
-
-  // rare second pass of this wave, from its own stage (all waves are past
-  // the ring once the barrier completes)
+  // rare second pass, with the true row maxima as references, for the waves
+  // that saw a score jump; the whole workgroup keeps the ring going
+  if (S.redo && lane == 0) s_redo = 1;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  if (S.redo) {
+  asm volatile("" ::: "memory");
+  if (uni(s_redo)) {
+    const bool mine = S.redo;
+    if (mine) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float mx = S.tmax[hb];
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
-      S.m[hb] = mx;
-      S.l[hb] = 0.f;
+      for (int hb = 0; hb < HB; ++hb) {
+        float mx = S.tmax[hb];
+        mx = wave_max_xor(mx, 16);
+        mx = wave_max_xor(mx, 32);
+        S.m[hb] = mx;
+        S.l[hb] = 0.f;
 #pragma unroll
-      for (int db = 0; db < DB; ++db) S.o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int db = 0; db < DB; ++db) S.o[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
-    S.redo = false;
-    for (int i = 0; i < n; ++i) {
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) issue_tile(a, ch.b, ch.len, k0 + i, w, ww, lane);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      compute_tile(a, S, w, (k0 + i) * kTile, lane);
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    }
+    run_pass<HB>(a, S, ch, k0, n, w, lane, mine);
   }
-  write_partial(a, S, slot, w, lane);
+  write_partial<HB>(a, S, slot, w, lane);
 }
+
+constexpr int kHB = MLA_DECODE_HB;
 
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s, int grid) {
-  hipLaunchKernelGGL(decode_bf16_kernel, dim3(grid), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(decode_bf16_kernel<kHB>, dim3(grid), dim3(Geo<kHB>::kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -19,9 +19,11 @@ constexpr int DR_MAX = 32;
 
 __global__ __launch_bounds__(128) void decode_f32_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int g = xcd_logical_id(blockIdx.x, gridDim.x);
   const int64_t nt = plan_total_tiles(a.seqlens, a.batch, a.row_groups, lane);
   if (nt == 0) return;
+  const int g = plan_chunk_of_block(
+      blockIdx.x, plan_chunks_before(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, lane));
+  if (g < 0) return;
   Chunk ch;
   if (!plan_find_chunk(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, g, lane, ch)) return;
   if (ch.c == 0 && threadIdx.x == 0) {

@@ -92,6 +92,19 @@ __device__ inline int64_t plan_total_tiles(const int32_t* seqlens, int batch, in
   return (int64_t)uni(part) * row_groups;
 }
 
+// The chunk number a decode workgroup runs, given the total chunk count C, or
+// -1 for none.  Workgroups are dealt to the 8 XCDs round-robin (block i to
+// XCD i % 8), so chunks are handed out to give every XCD the same share,
+// ceil(C / 8), consecutive chunk numbers on one XCD.  Needs a grid of at
+// least 8 * ceil(C / 8) workgroups.
+__device__ inline int plan_chunk_of_block(int block, int C) {
+  const int per = (C + 7) / 8;
+  const int k = block / 8;
+  if (k >= per) return -1;
+  const int g = (block % 8) * per + k;
+  return g < C ? g : -1;
+}
+
 // Chunks of all units of sequences [0, b_end) (the first chunk number of b_end).
 __device__ inline int plan_chunks_before(const int32_t* seqlens, int b_end, int row_groups,
                                          int64_t nt, int G, int lane) {
