@@ -16,6 +16,9 @@ its stream) and the CPU oracle timed on a bounded sample of the same workload.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import math
 import os
@@ -31,6 +34,100 @@ METRIC = "MLA decode latent-KV HBM GB/s + MFMA TFLOP/s vs roofline, B=64 L=4096"
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 MALL_BYTES = 256 * 2 ** 20
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "head_latent_attention_03_amd", "csrc")
+# sources that define the decode kernel; the traffic summary is valid only for them
+DECODE_SOURCES = {"bf16": ("decode_bf16.hip", "mla_common.hpp", "mla_internal.hpp"),
+                  "f32": ("decode_f32.hip", "mla_common.hpp", "mla_internal.hpp"),
+                  "fp8": ("decode_fp8.hip", "mla_common.hpp", "mla_internal.hpp")}
+DECODE_KERNEL_NAME = {"bf16": "decode_bf16_kernel", "f32": "decode_f32_kernel",
+                      "fp8": "decode_fp8_kernel"}
+
+
+def source_hash(kind):
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES[kind]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(kind, workload):
+    return os.path.join(PROFILES, f"{DECODE_KERNEL_NAME[kind]}_{workload}_hbm_traffic.txt")
+
+
+def read_traffic(kind, workload):
+    """HBM bytes per decode launch from the committed counter summary, or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = traffic_file(kind, workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_hash(kind):
+        return None
+    return int(vals["hbm_bytes_per_launch"])
+
+
+def _pmc_rows(path, counter):
+    rows = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            rows.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), 0.0)
+            rows[(r["Kernel_Name"], r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, kind, workload, copy_mib, commands):
+    """Write the traffic summary from a FETCH_SIZE run and a WRITE_SIZE run.
+
+    Both counters are KiB per dispatch.  Each is scaled by what it reads for
+    the plain device copy of copy_mib MiB in the same run (reads copy_mib MiB,
+    writes copy_mib MiB), so that the summary is in bytes of the copy's own
+    ruler."""
+    def load(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        return _pmc_rows(f[0], counter)
+    out = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = load(d, counter)
+        dec = {int(i): v for (k, i), v in rows.items() if DECODE_KERNEL_NAME[kind] in k}
+        # the calibration copy is the last device copy before the first decode
+        # (earlier copies are the cache replicas)
+        cpy = {int(i): v for (k, i), v in rows.items()
+               if "copyBuffer" in k and dec and int(i) < min(dec)}
+        if not dec or not cpy:
+            raise SystemExit(f"{counter}: decode or copy dispatches missing in {d}")
+        cpy_kib = cpy[max(cpy)]
+        dec = list(dec.values())
+        factor = copy_mib * 1024.0 / cpy_kib
+        out[counter] = (float(np.mean(dec)), cpy_kib, factor)
+    fetch_b = out["FETCH_SIZE"][0] * out["FETCH_SIZE"][2] * 1024
+    write_b = out["WRITE_SIZE"][0] * out["WRITE_SIZE"][2] * 1024
+    path = traffic_file(kind, workload)
+    with open(path, "w") as fh:
+        fh.write(f"# HBM traffic of {DECODE_KERNEL_NAME[kind]} on workload {workload}\n")
+        fh.write("# from two rocprofv3 counter runs (FETCH_SIZE, then WRITE_SIZE), KiB per dispatch,\n")
+        fh.write(f"# each scaled by the same counter on a plain {copy_mib} MiB device copy in the run\n")
+        for c in commands:
+            fh.write(f"# command: {c}\n")
+        for counter, (dec, cpy, factor) in out.items():
+            fh.write(f"{counter.lower()}_decode_kib_avg: {dec:.1f}\n")
+            fh.write(f"{counter.lower()}_copy_kib: {cpy:.1f}\n")
+            fh.write(f"{counter.lower()}_scale: {factor:.4f}\n")
+        fh.write(f"hbm_read_bytes_per_launch: {int(fetch_b)}\n")
+        fh.write(f"hbm_write_bytes_per_launch: {int(write_b)}\n")
+        fh.write(f"hbm_bytes_per_launch: {int(fetch_b + write_b)}\n")
+        fh.write(f"source_sha256_16: {source_hash(kind)}\n")
+    print(open(path).read())
 
 
 def _elt(dt):
@@ -97,7 +194,20 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the decode traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="command lines of the counter runs, recorded in the summary")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        from head_latent_attention_03_amd import inputs
+        spec = inputs.workload(args.config)
+        kind = "f32" if spec.act_dtype == "f32" else ("fp8" if spec.latent_dtype == "e4m3" else "bf16")
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], kind, spec.name,
+                      args.copy_calibration_mib, args.pmc_command)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
               "no multi-GPU path.  Run with --gpus 1.", file=sys.stderr)
@@ -120,6 +230,14 @@ def main():
         reps.append((db.kv_latent.clone(), None if db.kv_scale is None else db.kv_scale.clone(),
                      db.kv_rope.clone()))
     torch.cuda.synchronize()
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * 2 ** 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -158,6 +276,7 @@ def main():
     else:
         achieved, peak, unit = dec_f / (dec_ms * 1e-3) / 1e12, MFMA_PEAK_TFLOPS[kind], "TFLOP/s"
 
+    traffic = read_traffic(kind, spec.name)
     out = {
         "metric": METRIC,
         "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -187,7 +306,8 @@ def main():
             "peak": peak,
             "unit": unit,
             "frac": round(achieved / peak, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_over_algorithmic": None if traffic is None else round(traffic / dec_b, 4),
             "launch_ms": round(dec_ms, 5),
             "algorithmic_bytes": int(dec_b),
             "algorithmic_flops": int(dec_f),
