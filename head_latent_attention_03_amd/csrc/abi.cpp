@@ -19,7 +19,6 @@ using mla::CombineArgs;
 using mla::DecodeArgs;
 
 constexpr int kMaxQLen = 8;
-constexpr bool kHaveFp8Decode = false;
 constexpr int kMaxDevices = 64;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -46,7 +45,6 @@ mla_status_t check_dims(const mla_dims_t* d) {
   }
   if (act == MLA_BF16) {
     if (lat != MLA_BF16 && lat != MLA_FP8_E4M3) return MLA_ERR_BAD_DTYPE;
-    if (lat == MLA_FP8_E4M3 && !kHaveFp8Decode) return MLA_ERR_UNSUPPORTED;
     if (d->page_size != mla::kPage || d->d_latent != 512 || d->d_rope != 64 ||
         d->d_nope != 128 || d->d_v != 128)
       return MLA_ERR_UNSUPPORTED;
@@ -228,7 +226,7 @@ MLA_EXPORT mla_status_t mla_decode_paged(const mla_dims_t* dims, int32_t batch, 
   if (dims->act_dtype == MLA_F32) {
     e = mla::launch_decode_f32(la, s, L.grid);
   } else if (fp8) {
-    e = hipErrorNotSupported;
+    e = mla::launch_decode_fp8(la, s, L.grid);
   } else {
     e = mla::launch_decode_bf16(la, s, L.grid);
   }

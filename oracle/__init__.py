@@ -34,7 +34,8 @@ from .codecs import (bf16_bits_to_f64, f64_to_bf16_bits, e4m3_bits_to_f64,
                      f64_to_e4m3_bits, E4M3_MAX)
 from .mla import (rope_theta, apply_rope, gather_cache, expand_kv,
                   absorb_query, mla_decode_expanded, mla_decode_absorbed,
-                  decode_stored, DecodeResult, inputs_from_workload)
+                  decode_stored, DecodeResult, inputs_from_workload,
+                  quantize_rows_e4m3)
 from .cache_sizes import (mla_cache_elems_per_token, mha_cache_elems_per_token,
                           gqa_cache_elems_per_token, mqa_cache_elems_per_token,
                           gqa_equivalent_groups)
@@ -43,7 +44,8 @@ __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "e4m3_bits_to_f64",
     "f64_to_e4m3_bits", "E4M3_MAX", "rope_theta", "apply_rope", "gather_cache",
     "expand_kv", "absorb_query", "mla_decode_expanded", "mla_decode_absorbed",
-    "decode_stored", "DecodeResult", "inputs_from_workload", "mla_cache_elems_per_token",
+    "decode_stored", "DecodeResult", "inputs_from_workload", "quantize_rows_e4m3",
+    "mla_cache_elems_per_token",
     "mha_cache_elems_per_token", "gqa_cache_elems_per_token",
     "mqa_cache_elems_per_token", "gqa_equivalent_groups",
 ]

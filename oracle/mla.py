@@ -35,7 +35,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .codecs import bf16_bits_to_f64, e4m3_bits_to_f64
+from .codecs import bf16_bits_to_f64, e4m3_bits_to_f64, f64_to_e4m3_bits, E4M3_MAX
 
 
 def decode_stored(arr, dtype, scale=None):
@@ -148,7 +148,7 @@ def _visible(length, q_len, j, causal):
     return pos, max(int(n_vis), 0)
 
 
-def _decode(inputs, rows, return_probs, absorbed):
+def _decode(inputs, rows, return_probs, absorbed, query_e4m3=False):
     q_nope = inputs["q_nope"]
     q_rope = inputs["q_rope"]
     w_uk = inputs["w_uk"]
@@ -186,6 +186,8 @@ def _decode(inputs, rows, return_probs, absorbed):
         qc = q_nope[b, j, h]
         qr = apply_rope(q_rope[b, j, h], pos, base)
         q_lat = w_uk[h].T @ qc
+        if query_e4m3:
+            q_lat = quantize_rows_e4m3(q_lat)
         res.q_latent[i] = q_lat
         res.q_pe[i] = qr
         res.n_visible[i] = n_vis
@@ -234,12 +236,29 @@ def mla_decode_expanded(inputs, rows=None, return_probs=False):
     return _decode(inputs, rows, return_probs, absorbed=False)
 
 
-def mla_decode_absorbed(inputs, rows=None, return_probs=False):
+def mla_decode_absorbed(inputs, rows=None, return_probs=False, query_e4m3=False):
     """Absorbed form: s_t = scale * (q~ . c_t + q_pe . k^R_t), o = W_UV[h] (sum_t p_t c_t).
 
-    Used only to check absorption is exact ([LRKV] "Empirical Gains"; [SNAP]).
+    Checks that absorption is exact ([LRKV] "Empirical Gains"; [SNAP]).  With
+    ``query_e4m3`` the absorbed query is first replaced by its per-row e4m3
+    form (``quantize_rows_e4m3``), the form an fp8-cache decode multiplies
+    with the e4m3 cache ([LKVC] "FP8/FP32 Mixed Precision").
     """
-    return _decode(inputs, rows, return_probs, absorbed=True)
+    return _decode(inputs, rows, return_probs, absorbed=True, query_e4m3=query_e4m3)
+
+
+def quantize_rows_e4m3(x):
+    """Each row of x as OCP e4m3 codes times one per-row scale, decoded back.
+
+    The scale is max|row| / 448, so the row's largest magnitude maps to the
+    largest finite e4m3 value (1 for an all-zero row); codes are rounded to
+    nearest-even by this package's own encoder.  Pinned against torch's
+    float8_e4m3fn cast and the e4m3 rounding bound in the tests.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.max(np.abs(x), axis=-1, keepdims=True)
+    scale = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    return e4m3_bits_to_f64(f64_to_e4m3_bits(x / scale)) * scale
 
 
 def inputs_from_workload(wl, latent_override=None):

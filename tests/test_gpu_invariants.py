@@ -69,6 +69,57 @@ def test_needle_gather_is_bit_exact():
             assert np.array_equal(got[b, 0, h], want), (b, h, t)
 
 
+def test_needle_gather_fp8_is_bit_exact():
+    """The needle test through the e4m3 cache path, with every token scale 1.
+
+    Latent codes are e4m3: 1.0 (0x38) one-hots of the base-16 digits of t in
+    dims [0, 64) and a random finite e4m3 payload after.  The absorbed query
+    is stored as e4m3 1.0 at the target's one-hot positions with row scale
+    2048, so scores are exact and every other token's weight is exactly 0;
+    the latent output must equal the target's stored payload (exact in bf16).
+    """
+    seqlens = [4096, 3000, 777, 64, 1]
+    spec = inputs.workload(4, batch=len(seqlens), seqlen=seqlens)
+    wl = inputs.make_workload(spec)
+    rng = np.random.default_rng(15)
+    lat = wl.kv_latent.copy()
+    pay = torch.from_numpy(np.clip(rng.standard_normal(8 * 448).astype(np.float32) * 40, -400, 400)) \
+        .to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(8, 448)
+    for b, L in enumerate(seqlens):
+        for t in range(L):
+            p, sl = wl.block_table[b, t // 64], t % 64
+            code = np.zeros(64, dtype=np.uint8)
+            for k in range(4):
+                code[16 * k + ((t >> (4 * k)) & 15)] = 0x38
+            lat[p, sl, :64] = code
+            lat[p, sl, 64:] = pay[(t * 7 + b) % 8]
+    wl.kv_latent = lat
+    wl.kv_scale = np.ones_like(wl.kv_scale)
+    db = DeviceBatch.from_workload(wl, "cuda:0")
+    H = spec.n_heads
+    target = np.zeros((len(seqlens), H), dtype=np.int64)
+    ql = np.zeros((len(seqlens), 1, H, 512), dtype=np.uint8)
+    for b, L in enumerate(seqlens):
+        for h in range(H):
+            t = (h * 2654435761 + b * 97) % L
+            target[b, h] = t
+            for k in range(4):
+                ql[b, 0, h, 16 * k + ((t >> (4 * k)) & 15)] = 0x38
+    db.q_latent.copy_(torch.from_numpy(ql).view(torch.float8_e4m3fn))
+    db.q_latent_scale.fill_(2048.0)
+    db.q_pe.zero_()
+    db.decode()
+    db.combine(with_uv=False)
+    torch.cuda.synchronize()
+    got = db.out_latent.float().cpu().numpy()
+    for b, L in enumerate(seqlens):
+        for h in range(H):
+            t = target[b, h]
+            want = torch.from_numpy(lat[wl.block_table[b, t // 64], t % 64].copy()) \
+                .view(torch.float8_e4m3fn).float().numpy()
+            assert np.array_equal(got[b, 0, h], want), (b, h, t)
+
+
 def test_page_permutation_is_bit_identical():
     """Moving pages in HBM (and the block table with them) changes no output bit."""
     spec = inputs.workload(2, batch=4, seqlen=[4096, 1000, 65, 2500])

@@ -51,6 +51,39 @@ def test_long_context_reduced():
     _run_check(inputs.workload(3, batch=2, seqlen=[20000, 9000]))
 
 
+@pytest.mark.parametrize("seqlens", [[1], [65, 300, 31], [64, 128, 2, 5000]])
+def test_fp8_cache_reduced_ragged(seqlens):
+    """e4m3 latent with per-token scales, short and ragged lengths, 6e-2 against the
+    dequantised cache."""
+    _run_check(inputs.workload(4, batch=len(seqlens), seqlen=seqlens))
+
+
+@pytest.mark.parametrize("softmax_scale", [2.0, 8.0])
+def test_fp8_cache_peaked_softmax(softmax_scale):
+    """e4m3 latent with a large softmax scale: peaked rows whose maximum grows from
+    tile to tile, so the running reference moves and the accumulator is rescaled.
+
+    At this sharpness the e4m3 query alone moves scores by ~2^-4 relative, so the
+    reference is the oracle's absorbed form with the same per-row e4m3 query; the
+    end-to-end checks against the exact query are the other fp8 tests."""
+    _run_check(inputs.workload(4, batch=3, seqlen=[700, 4096, 33], init="fan_in",
+                               softmax_scale=softmax_scale), query_e4m3=True)
+
+
+def test_fp8_cache_two_query_tokens():
+    """e4m3 latent, two causal query tokens per sequence."""
+    _run_check(inputs.workload(4, batch=4, q_len=2, seqlen=[2, 65, 300, 1000], init="fan_in"))
+
+
+def test_full_size_fp8_sampled():
+    """The B=64, L=4096 e4m3-cache workload at full size, sampled rows."""
+    spec = inputs.workload(4)
+    wl = inputs.make_workload(spec)
+    got = run_library(wl)
+    check_against_oracle(wl, got, rows=sample_rows(wl, 12, seed=4))
+    assert np.all(np.isfinite(got["out"])) and np.all(np.isfinite(got["out_latent"]))
+
+
 def test_full_size_b64_l4096_sampled():
     """The B=64, L=4096 bf16 workload at full size, sampled rows."""
     spec = inputs.workload(2)

@@ -227,3 +227,26 @@ def test_row_subset_matches_full_run():
         k = (b * 2 + j) * 4 + h
         assert np.array_equal(sub.out[i], full.out[k])
         assert np.array_equal(sub.o_latent[i], full.o_latent[k])
+
+
+def test_absorbed_with_e4m3_query_moves_only_through_the_query():
+    """With query_e4m3 the absorbed decode equals the absorbed decode fed the quantised
+    query by hand (it changes nothing else), and it differs from the exact one."""
+    from oracle_io import random_inputs
+    rng = np.random.default_rng(41)
+    inp = random_inputs(rng, batch=2, q_len=2, n_heads=3, d_c=32, d_rope=8, d_nope=16,
+                        d_v=16, seqlens=[70, 9], page_size=16)
+    a = oracle.mla_decode_absorbed(inp, query_e4m3=True)
+    exact = oracle.mla_decode_absorbed(inp)
+    # redo by hand: quantise q~, then the plain absorbed softmax
+    for i, (b, j, h) in enumerate(a.rows):
+        q8 = oracle.quantize_rows_e4m3(inp["w_uk"][h].T @ inp["q_nope"][b, j, h])
+        assert np.allclose(a.q_latent[i], q8, rtol=0, atol=1e-15)
+        c, kr = oracle.gather_cache(inp["kv_latent"], inp["kv_rope"], inp["block_table"],
+                                    int(b), int(inp["seqlens"][b]), inp["page_size"])
+        n = int(a.n_visible[i])
+        s = inp["softmax_scale"] * (c[:n] @ q8 + kr[:n] @ a.q_pe[i])
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        assert np.allclose(a.o_latent[i], p @ c[:n], rtol=1e-12, atol=1e-14)
+    assert not np.allclose(a.o_latent, exact.o_latent, rtol=1e-6, atol=0)
