@@ -81,16 +81,15 @@ __device__ __forceinline__ u32x8 u32x8_of(u32x4 lo, u32x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// This wave's 4 DMA instructions for tile k: latent rows of tokens
-// 4w..4w+3 (two 1 KiB copies), their rotary rows (32 lanes) and their 4
-// scales (one lane).  Latent and rotary rows past the sequence end re-read
-// its last token; the scales of such tokens are whatever the page holds and
-// are never used unmasked.
-__device__ __forceinline__ void issue_tile(const DecodeArgs& a, int b, int len, int k, int st,
+// This wave's 4 DMA instructions for tile k, whose first token sits in
+// physical page `page`: latent rows of tokens 4w..4w+3 (two 1 KiB copies),
+// their rotary rows (32 lanes) and their 4 scales (one lane).  Latent and
+// rotary rows past the sequence end re-read its last token; the scales of
+// such tokens are whatever the page holds and are never used unmasked.
+__device__ __forceinline__ void issue_tile(const DecodeArgs& a, int page, int len, int k, int st,
                                            int w, int lane) {
   const int tok0 = k * kTile;
   const int last = len - 1;
-  const int page = sload_i32(a.block_table + (int64_t)b * a.max_pages, tok0 / kPage);
   const int64_t row0 = (int64_t)page * kPage + (tok0 % kPage);
   const uint8_t* lat = (const uint8_t*)a.kv_lat + row0 * LAT_ROW;
   const uint8_t* rope = (const uint8_t*)a.kv_rope + row0 * ROPE_ROW;
@@ -101,16 +100,15 @@ __device__ __forceinline__ void issue_tile(const DecodeArgs& a, int b, int len, 
     const int t = w * 4 + 2 * j + (lane >> 5);
     const int tc = min(tok0 + t, last) - tok0;
     const uint32_t off = (uint32_t)(tc * LAT_ROW + (((lane & 31) ^ lat8_key(t)) << 4));
-    dma16(lat + off, dst + (w * 4 + 2 * j) * LAT_ROW);
+    dma16_s(lat, off, dst + (w * 4 + 2 * j) * LAT_ROW);
   }
   {
     const int t = w * 4 + (lane >> 3);
     const int tc = min(tok0 + t, last) - tok0;
     const uint32_t off = (uint32_t)(tc * ROPE_ROW + (((lane & 7) ^ rope_key(t)) << 4));
-    if (lane < 32) dma16(rope + off, dst + ROPE_OFF + w * 4 * ROPE_ROW);
+    if (lane < 32) dma16_s(rope, off, dst + ROPE_OFF + w * 4 * ROPE_ROW);
   }
-  if (lane == 0)
-    dma16(a.kv_scale + row0 + w * 4, dst + SCALE_OFF + w * 16);
+  if (lane == 0) dma16_s(a.kv_scale + row0 + w * 4, 0u, dst + SCALE_OFF + w * 16);
 }
 
 template <int N>
@@ -337,10 +335,20 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_fp8_kernel(DecodeArgs a) {
   S.l = 0.f;
   S.lim = valid ? (a.causal ? ch.len - a.q_len + j + 1 : ch.len) : 0;
 
+  // page indices of the chunk, one per lane (a window of 64)
+  const int32_t* bt_row = a.block_table + (int64_t)ch.b * a.max_pages;
+  PageWindow W;
+  W.pg0 = uni(k0 * kTile / kPage);
+  W.v = page_window_load(bt_row, a.max_pages, W.pg0, lane);
+  auto issue = [&](int k, int st) {
+    issue_tile(a, page_lookup(W, bt_row, a.max_pages, k * kTile / kPage, lane), ch.len, k, st, w,
+               lane);
+  };
+
   // prologue: AHEAD tiles in flight
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i)
-    if (i < n) issue_tile(a, ch.b, ch.len, k0 + i, i, w, lane);
+    if (i < n) issue(k0 + i, i);
 
   // s_ref: the largest token scale of the chunk (every wave forms it alone)
   float sref = 0.f;
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_fp8_kernel(DecodeArgs a) {
     wait_tiles(n - 1 - i);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (i + AHEAD < n) issue_tile(a, ch.b, ch.len, k0 + i + AHEAD, (i + AHEAD) % NSTAGE, w, lane);
+    if (i + AHEAD < n) issue(k0 + i + AHEAD, (i + AHEAD) % NSTAGE);
     compute_tile(a, S, i % NSTAGE, (k0 + i) * kTile, lane, lo, inv_sref, sref_256);
   }
 

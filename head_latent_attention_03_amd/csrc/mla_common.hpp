@@ -70,18 +70,6 @@ __device__ inline float wave_sum_xor(float v, int mask) {
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Scalar (SMEM) load of a wave-uniform int, with its wait in the same asm
-// block.  Used for block-table lookups inside pipelined loops: a vector load
-// there would make the compiler drain every outstanding global->LDS copy.
-__device__ __forceinline__ int sload_i32(const int32_t* base, int idx) {
-  int v;
-  asm volatile("s_load_dword %0, %1, %2\n\ts_waitcnt lgkmcnt(0)"
-               : "=s"(v)
-               : "s"(base), "s"(idx * 4)
-               : "memory");
-  return v;
-}
-
 // Total tiles NT over all units (every lane gets the same value).
 __device__ inline int64_t plan_total_tiles(const int32_t* seqlens, int batch, int row_groups,
                                            int lane) {
@@ -190,6 +178,53 @@ __device__ __forceinline__ void dma16(const void* gsrc, const MLA_LDS uint8_t* l
                :
                : "s"(m0), "v"(gsrc)
                : "memory", "m0");
+}
+
+
+// The same copy from a wave-uniform base address held in SGPRs plus a 32-bit
+// per-lane byte offset (global_load_lds's saddr form: no 64-bit address
+// arithmetic per lane).
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff,
+                                        const MLA_LDS uint8_t* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  // (readfirstlane returns int: each half goes through uint32_t so that the
+  // low half is zero-extended, never sign-extended into the high half)
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"((const void*)(uintptr_t)bu)
+               : "memory", "m0");
+}
+
+// A window of 64 consecutive entries of one sequence's block table, one per
+// lane, so that a tile's physical page is a v_readlane (no memory latency on
+// the copy-issue path).  Pages are looked up in increasing order; a lookup
+// past the window reloads it (a plain vector load, which waits for the
+// wave's outstanding copies: once per 64 pages).
+struct PageWindow {
+  int v;     // lane l: block_table[b][pg0 + l] (0 past the row)
+  int pg0;
+};
+
+__device__ inline int page_window_load(const int32_t* bt_row, int max_pages, int pg0, int lane) {
+  const int p = pg0 + lane;
+  return p < max_pages ? bt_row[p] : 0;
+}
+
+__device__ __forceinline__ int page_lookup(PageWindow& W, const int32_t* bt_row, int max_pages,
+                                           int pg, int lane) {
+  int page;
+  if (uni(pg - W.pg0) >= 64) {
+    W.pg0 = uni(pg);
+    W.v = page_window_load(bt_row, max_pages, W.pg0, lane);
+    page = __builtin_amdgcn_readlane(W.v, 0);
+  } else {
+    page = __builtin_amdgcn_readlane(W.v, uni(pg - W.pg0));
+  }
+  return page;
 }
 
 }  // namespace mla
