@@ -46,6 +46,7 @@ __device__ __forceinline__ double rope_theta(int i, int d_rope, float base) {
 constexpr int AB_M = 64;
 constexpr int AB_K = 128;    // d_nope
 constexpr int AB_N = 512;    // d_lat
+constexpr int AB_ROPE = 64;  // d_rope
 
 template <int NB, bool FP8>
 __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
@@ -55,7 +56,6 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
   constexpr int NBLK = NB / 16 / 4;            // 16-column blocks per wave
   __shared__ __attribute__((aligned(16))) uint8_t s_w[AB_K * PITCH];
   __shared__ float s_amax[4][AB_M];
-  __shared__ double s_theta[64];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -67,8 +67,9 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
   const int mb = blk % nmb;
   const int m_total = a.batch * a.q_len;
 
-  // stage W_UK[h][:, cb*NB .. +NB] (row k = content coordinate); all loads
-  // are issued before the first store
+  // every global load of the workgroup is issued before the first use:
+  // the W_UK[h][:, cb*NB .. +NB] slice (row k = content coordinate), the q^C
+  // rows (B operand) and this block's share of the rotary rows
   const uint16_t* W = (const uint16_t*)a.w_uk + (int64_t)h * AB_K * AB_N + cb * NB;
   constexpr int CHUNKS = AB_K * NB / 8;        // 16-byte chunks
   constexpr int PER_T = CHUNKS / 256;
@@ -79,32 +80,6 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
     const int row = c / (NB / 8), col = c % (NB / 8);
     stage[i] = *(const u32x4*)&W[(int64_t)row * AB_N + col * 8];
   }
-#pragma unroll
-  for (int i = 0; i < PER_T; ++i) {
-    const int c = threadIdx.x + i * 256;
-    const int row = c / (NB / 8), col = c % (NB / 8);
-    *(u32x4*)&s_w[row * PITCH + col * 16] = stage[i];
-  }
-
-  // rotary part (column block 0 only): 64 rows x d_rope/2 pairs
-  if (cb == 0) {
-    if (threadIdx.x < a.d_rope / 2 && threadIdx.x < 64)
-      s_theta[threadIdx.x] = rope_theta(threadIdx.x, a.d_rope, a.rope_base);
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < AB_M * (a.d_rope / 2); idx += 256) {
-      const int ml = idx / (a.d_rope / 2), i = idx % (a.d_rope / 2);
-      const int m = mb * AB_M + ml;
-      if (m >= m_total) continue;
-      const int b = m / a.q_len, j = m % a.q_len;
-      const int pos = a.seqlens[b] - a.q_len + j;
-      const int64_t off = ((int64_t)m * a.n_heads + h) * a.d_rope + 2 * i;
-      const uint16_t* qr = (const uint16_t*)a.q_rope + off;
-      float y0, y1;
-      rope_pair(bf16_bits_to_f32(qr[0]), bf16_bits_to_f32(qr[1]), pos, s_theta[i], y0, y1);
-      *(uint32_t*)((uint16_t*)a.q_pe + off) = pack_bf16x2(y0, y1);
-    }
-  }
-
   // B operand: q^C rows (m = lr within 16-row block y), k = kk*32 + lg*8 ..
   u16x8 qb[4][AB_K / 32];
 #pragma unroll
@@ -116,6 +91,46 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
     for (int kk = 0; kk < AB_K / 32; ++kk) {
       const u16x8 v = *(const u16x8*)(q + kk * 32 + lg * 8);
       qb[y][kk] = valid ? v : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  // rotary part: the NCB column blocks of a head split its 64 rows; thread t
+  // rotates pair t % 32 of rows (t + 256 e) / 32 of this block's share
+  constexpr int PAIRS = AB_ROPE / 2;
+  constexpr int RROWS = AB_M / NCB;
+  constexpr int RPER = (RROWS * PAIRS + 255) / 256;
+  uint32_t rq[RPER];
+  int rpos[RPER];
+  bool rvalid[RPER];
+#pragma unroll
+  for (int e = 0; e < RPER; ++e) {
+    const int idx = threadIdx.x + e * 256;
+    const int m = mb * AB_M + cb * RROWS + idx / PAIRS;
+    const bool valid = idx < RROWS * PAIRS && m < m_total;
+    const int mm = valid ? m : 0;
+    const int64_t off = ((int64_t)mm * a.n_heads + h) * AB_ROPE + 2 * (idx % PAIRS);
+    rq[e] = *(const uint32_t*)((const uint16_t*)a.q_rope + off);
+    // (a position may be negative when a sequence holds fewer than q_len tokens)
+    rpos[e] = a.seqlens[mm / a.q_len] - a.q_len + mm % a.q_len;
+    rvalid[e] = valid;
+  }
+#pragma unroll
+  for (int i = 0; i < PER_T; ++i) {
+    const int c = threadIdx.x + i * 256;
+    const int row = c / (NB / 8), col = c % (NB / 8);
+    *(u32x4*)&s_w[row * PITCH + col * 16] = stage[i];
+  }
+  {
+    const double theta = rope_theta(threadIdx.x % PAIRS, AB_ROPE, a.rope_base);
+#pragma unroll
+    for (int e = 0; e < RPER; ++e) {
+      if (!rvalid[e]) continue;
+      const int idx = threadIdx.x + e * 256;
+      const int m = mb * AB_M + cb * RROWS + idx / PAIRS;
+      const int64_t off = ((int64_t)m * a.n_heads + h) * AB_ROPE + 2 * (idx % PAIRS);
+      float y0, y1;
+      rope_pair(__uint_as_float(rq[e] << 16), __uint_as_float(rq[e] & 0xffff0000u), rpos[e],
+                theta, y0, y1);
+      *(uint32_t*)((uint16_t*)a.q_pe + off) = pack_bf16x2(y0, y1);
     }
   }
   __syncthreads();

@@ -20,27 +20,29 @@ namespace {
 // decode pass recorded them (a sequence with no cached token has no chunk).
 __device__ __forceinline__ void unit_slots(const CombineArgs& a, int b, int rg, int& first,
                                            int& count) {
-  if (a.seqlens[b] <= 0) {
-    first = 0;
-    count = 0;
-    return;
-  }
   const int64_t u = (int64_t)b * a.row_groups + rg;
-  first = a.unit_chunks[2 * u];
-  count = a.unit_chunks[2 * u + 1];
+  const int len = a.seqlens[b];
+  const int f = a.unit_chunks[2 * u];
+  const int c = a.unit_chunks[2 * u + 1];
+  first = len > 0 ? f : 0;
+  count = len > 0 ? c : 0;
 }
 
-// Merge one 64-dim slice [64 sl, 64 sl + 64) of one row's partials (one
-// thread).  Partials are bf16 when the activations are bf16 and f32
-// otherwise.  Returns the row's log-sum-exp (-inf: no visible key, acc = 0).
-constexpr int SLICE = 64;
+// Merge the slice [W sl, W sl + W) of one row's partials (one thread).
+// Partials are bf16 when the activations are bf16 and f32 otherwise.  The
+// log-sum-exps of up to 8 splits, then the slices of up to 4 splits, are
+// loaded together before any arithmetic uses them.  Returns the row's
+// log-sum-exp (-inf: no visible key, acc = 0).
+constexpr int LSE_GROUP = 8;
+constexpr int PART_GROUP = 4;
 
+template <int W>
 __device__ __forceinline__ void load_slice(const CombineArgs& a, int64_t slot, int r, int sl,
-                                           float (&v)[SLICE]) {
+                                           float (&v)[W]) {
   if (a.out_dtype == DT_BF16) {
-    const uint16_t* src = (const uint16_t*)a.part_o + (slot * kRowsPerWG + r) * a.d_lat + sl * SLICE;
+    const uint16_t* src = (const uint16_t*)a.part_o + (slot * kRowsPerWG + r) * a.d_lat + sl * W;
 #pragma unroll
-    for (int c = 0; c < SLICE / 8; ++c) {
+    for (int c = 0; c < W / 8; ++c) {
       const u32x4 u = *(const u32x4*)(src + c * 8);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -49,9 +51,9 @@ __device__ __forceinline__ void load_slice(const CombineArgs& a, int64_t slot, i
       }
     }
   } else {
-    const float* src = (const float*)a.part_o + (slot * kRowsPerWG + r) * a.d_lat + sl * SLICE;
+    const float* src = (const float*)a.part_o + (slot * kRowsPerWG + r) * a.d_lat + sl * W;
 #pragma unroll
-    for (int c = 0; c < SLICE / 4; ++c) {
+    for (int c = 0; c < W / 4; ++c) {
       const f32x4 u = *(const f32x4*)(src + c * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[c * 4 + e] = u[e];
@@ -59,72 +61,97 @@ __device__ __forceinline__ void load_slice(const CombineArgs& a, int64_t slot, i
   }
 }
 
+template <int W>
 __device__ __forceinline__ float merge_slice(const CombineArgs& a, int first, int count, int r,
-                                             int sl, float (&acc)[SLICE]) {
+                                             int sl, float (&acc)[W]) {
 #pragma unroll
-  for (int e = 0; e < SLICE; ++e) acc[e] = 0.f;
+  for (int e = 0; e < W; ++e) acc[e] = 0.f;
   float mx = -INFINITY;
-  for (int s = 0; s < count; ++s)
-    mx = fmaxf(mx, a.part_lse[(int64_t)(first + s) * kRowsPerWG + r]);
+  for (int s0 = 0; s0 < count; s0 += LSE_GROUP) {
+    float ls[LSE_GROUP];
+#pragma unroll
+    for (int s = 0; s < LSE_GROUP; ++s)
+      ls[s] = (s0 + s < count) ? a.part_lse[(int64_t)(first + s0 + s) * kRowsPerWG + r] : -INFINITY;
+#pragma unroll
+    for (int s = 0; s < LSE_GROUP; ++s) mx = fmaxf(mx, ls[s]);
+  }
   if (mx == -INFINITY) return -INFINITY;
   float tot = 0.f;
-  for (int s = 0; s < count; ++s) {
-    const float ls = a.part_lse[(int64_t)(first + s) * kRowsPerWG + r];
-    if (ls == -INFINITY) continue;
-    const float wgt = __expf(ls - mx);
-    tot += wgt;
-    float v[SLICE];
-    load_slice(a, first + s, r, sl, v);
+  for (int s0 = 0; s0 < count; s0 += PART_GROUP) {
+    float wgt[PART_GROUP];
+    float v[PART_GROUP][W];
 #pragma unroll
-    for (int e = 0; e < SLICE; ++e) acc[e] += wgt * v[e];
+    for (int s = 0; s < PART_GROUP; ++s) {
+      const bool in = s0 + s < count;
+      const int64_t slot = first + (in ? s0 + s : 0);
+      const float ls = in ? a.part_lse[slot * kRowsPerWG + r] : -INFINITY;
+      load_slice<W>(a, slot, r, sl, v[s]);
+      // a split with no visible key (or past the count) weighs exactly 0
+      wgt[s] = ls == -INFINITY ? 0.f : __expf(ls - mx);
+    }
+#pragma unroll
+    for (int s = 0; s < PART_GROUP; ++s) {
+      tot += wgt[s];
+#pragma unroll
+      for (int e = 0; e < W; ++e) acc[e] += wgt[s] == 0.f ? 0.f : wgt[s] * v[s][e];
+    }
   }
   const float inv = 1.0f / tot;
 #pragma unroll
-  for (int e = 0; e < SLICE; ++e) acc[e] *= inv;
+  for (int e = 0; e < W; ++e) acc[e] *= inv;
   return mx + __logf(tot);
 }
 
-// out = o~ (latent output): a workgroup merges 32 rows, thread = (row, slice).
+// out = o~ (latent output): a workgroup merges 32 rows, thread = (row, slice
+// of LAT_SLICE dims), 512 threads.  LAT_SLICE is 32 for the bf16 path
+// (d_lat = 512) and 16 for the f32 path (d_lat a multiple of 16 up to 128),
+// so every slice lies inside the row.
 constexpr int ROWS_PER_WG = 32;
 
-__global__ __launch_bounds__(256) void combine_latent_kernel(CombineArgs a) {
-  const int ml = threadIdx.x / 8, sl = threadIdx.x % 8;
+template <int LAT_SLICE>
+__global__ __launch_bounds__(512) void combine_latent_kernel(CombineArgs a) {
+  const int per_row = 512 / ROWS_PER_WG;       // slices per row (16)
+  const int ml = threadIdx.x / per_row, sl = threadIdx.x % per_row;
   const int64_t row = (int64_t)blockIdx.x * ROWS_PER_WG + ml;
   const int64_t rows = (int64_t)a.batch * a.q_len * a.n_heads;
-  if (row >= rows || sl * SLICE >= a.d_lat) return;
+  if (row >= rows || sl * LAT_SLICE >= a.d_lat) return;
   const int b = (int)(row / ((int64_t)a.q_len * a.n_heads));
   const int jh = (int)(row % ((int64_t)a.q_len * a.n_heads));
   int first, count;
   unit_slots(a, b, jh / kRowsPerWG, first, count);
-  float acc[SLICE];
-  const float lse = merge_slice(a, first, count, jh % kRowsPerWG, sl, acc);
+  float acc[LAT_SLICE];
+  const float lse = merge_slice<LAT_SLICE>(a, first, count, jh % kRowsPerWG, sl, acc);
   if (a.out_dtype == DT_BF16) {
-    uint16_t* o = (uint16_t*)a.out + row * a.d_lat + sl * SLICE;
+    uint16_t* o = (uint16_t*)a.out + row * a.d_lat + sl * LAT_SLICE;
 #pragma unroll
-    for (int c = 0; c < SLICE / 8; ++c)
+    for (int c = 0; c < LAT_SLICE / 8; ++c)
       *(u32x4*)(o + c * 8) = u32x4{pack_bf16x2(acc[c * 8], acc[c * 8 + 1]),
                                    pack_bf16x2(acc[c * 8 + 2], acc[c * 8 + 3]),
                                    pack_bf16x2(acc[c * 8 + 4], acc[c * 8 + 5]),
                                    pack_bf16x2(acc[c * 8 + 6], acc[c * 8 + 7])};
   } else {
-    float* o = (float*)a.out + row * a.d_lat + sl * SLICE;
+    float* o = (float*)a.out + row * a.d_lat + sl * LAT_SLICE;
 #pragma unroll
-    for (int c = 0; c < SLICE / 4; ++c)
+    for (int c = 0; c < LAT_SLICE / 4; ++c)
       *(f32x4*)(o + c * 4) = f32x4{acc[c * 4], acc[c * 4 + 1], acc[c * 4 + 2], acc[c * 4 + 3]};
   }
   if (a.lse != nullptr && sl == 0) a.lse[row] = lse;
 }
 
 // bf16: out[m, h, :] = W_UV[h] o~[m, h, :] for a block of 32 rows m = (b, j)
-// of one head.  Merged rows go to LDS as bf16; the product runs on
-// v_mfma_f32_16x16x32_bf16 as D^T = W_UV[h] o~^T, A = W rows (global, 16-byte
-// loads), B = o~ rows (LDS).
+// of one head, 8 waves.  Each wave first issues the loads of its W_UV
+// operands (16 rows n, all 512 k), which then stream in while the workgroup
+// merges its rows (thread = (row, 32-dim slice)) into LDS as bf16.  The
+// product runs on v_mfma_f32_16x16x32_bf16 as D^T = W_UV[h] o~^T: A = W rows
+// (registers), B = o~ rows (LDS).
 constexpr int UV_M = 32;
 constexpr int UV_DLAT = 512;
 constexpr int UV_DV = 128;
+constexpr int UV_SLICE = 32;
+constexpr int UV_PITCH = UV_DLAT + 8;        // bf16 elements per LDS row
 
-__global__ __launch_bounds__(256) void combine_uv_bf16_kernel(CombineArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_o[UV_M][UV_DLAT + 8];
+__global__ __launch_bounds__(512) void combine_uv_bf16_kernel(CombineArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_o[UV_M][UV_PITCH];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -135,69 +162,65 @@ __global__ __launch_bounds__(256) void combine_uv_bf16_kernel(CombineArgs a) {
   const int mb = blk % nmb;
   const int m_total = a.batch * a.q_len;
 
-  // 1. merge the block's rows into LDS: thread = (row, 64-dim slice)
+  // 0. this wave's A operands: W_UV[h] rows n = 16w + lr, k = 32kk + 8lg ..
+  const uint16_t* W = (const uint16_t*)a.w_uv + (int64_t)h * UV_DV * UV_DLAT;
+  u16x8 wa[UV_DLAT / 32];
+#pragma unroll
+  for (int kk = 0; kk < UV_DLAT / 32; ++kk)
+    wa[kk] = *(const u16x8*)(W + (int64_t)(w * 16 + lr) * UV_DLAT + kk * 32 + lg * 8);
+
+  // 1. merge the block's rows into LDS: thread = (row, 32-dim slice)
   {
-    const int ml = threadIdx.x / 8, sl = threadIdx.x % 8;
+    const int ml = threadIdx.x / (UV_DLAT / UV_SLICE), sl = threadIdx.x % (UV_DLAT / UV_SLICE);
     const int m = mb * UV_M + ml;
-    float acc[SLICE];
+    float acc[UV_SLICE];
     float lse = -INFINITY;
     if (m < m_total) {
       const int b = m / a.q_len, j = m % a.q_len;
       const int jh = j * a.n_heads + h;
       int first, count;
       unit_slots(a, b, jh / kRowsPerWG, first, count);
-      lse = merge_slice(a, first, count, jh % kRowsPerWG, sl, acc);
+      lse = merge_slice<UV_SLICE>(a, first, count, jh % kRowsPerWG, sl, acc);
     } else {
 #pragma unroll
-      for (int e = 0; e < SLICE; ++e) acc[e] = 0.f;
+      for (int e = 0; e < UV_SLICE; ++e) acc[e] = 0.f;
     }
 #pragma unroll
-    for (int c = 0; c < SLICE / 8; ++c)
-      *(u32x4*)&s_o[ml][sl * SLICE + c * 8] =
+    for (int c = 0; c < UV_SLICE / 8; ++c)
+      *(u32x4*)&s_o[ml][sl * UV_SLICE + c * 8] =
           u32x4{pack_bf16x2(acc[c * 8], acc[c * 8 + 1]), pack_bf16x2(acc[c * 8 + 2], acc[c * 8 + 3]),
                 pack_bf16x2(acc[c * 8 + 4], acc[c * 8 + 5]), pack_bf16x2(acc[c * 8 + 6], acc[c * 8 + 7])};
     if (a.lse != nullptr && sl == 0 && m < m_total) a.lse[(int64_t)m * a.n_heads + h] = lse;
   }
   __syncthreads();
 
-  // 2. D^T[n, m] = sum_k W[h, n, k] o~[m, k]; wave w: n blocks 2w, 2w+1; m blocks 0, 1
-  const uint16_t* W = (const uint16_t*)a.w_uv + (int64_t)h * UV_DV * UV_DLAT;
-  f32x4 acc[2][2];
+  // 2. D^T[n, m] = sum_k W[h, n, k] o~[m, k]; wave w: n block w, m blocks 0, 1
+  f32x4 acc[2];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int y = 0; y < 2; ++y) acc[y] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
   for (int kk = 0; kk < UV_DLAT / 32; ++kk) {
-    u16x8 wa[2], ob[2];
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
-      wa[x] = *(const u16x8*)(W + (int64_t)((2 * w + x) * 16 + lr) * UV_DLAT + kk * 32 + lg * 8);
-#pragma unroll
-    for (int y = 0; y < 2; ++y) ob[y] = *(const u16x8*)&s_o[y * 16 + lr][kk * 32 + lg * 8];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16_16x16x32(wa[x], ob[y], acc[x][y]);
+    for (int y = 0; y < 2; ++y) {
+      const u16x8 ob = *(const u16x8*)&s_o[y * 16 + lr][kk * 32 + lg * 8];
+      acc[y] = mfma_bf16_16x16x32(wa[kk], ob, acc[y]);
+    }
   }
-  // lane holds D^T[n = nblk*16 + lg*4 + r][m = mblk*16 + lr]
+  // lane holds D^T[n = 16w + lg*4 + r][m = mblk*16 + lr]
 #pragma unroll
   for (int y = 0; y < 2; ++y) {
     const int m = mb * UV_M + y * 16 + lr;
     if (m >= m_total) continue;
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int n0 = (2 * w + x) * 16 + lg * 4;
-      uint16_t* o = (uint16_t*)a.out + ((int64_t)m * a.n_heads + h) * UV_DV + n0;
-      *(u32x2*)o = u32x2{pack_bf16x2(acc[x][y][0], acc[x][y][1]),
-                         pack_bf16x2(acc[x][y][2], acc[x][y][3])};
-    }
+    const int n0 = w * 16 + lg * 4;
+    uint16_t* o = (uint16_t*)a.out + ((int64_t)m * a.n_heads + h) * UV_DV + n0;
+    *(u32x2*)o = u32x2{pack_bf16x2(acc[y][0], acc[y][1]), pack_bf16x2(acc[y][2], acc[y][3])};
   }
 }
 
 // f32 (small shapes: d_lat <= 512, d_v <= 128): one workgroup per (head, 32 rows),
 // merged rows in LDS, plain fp32 FMAs.
 __global__ __launch_bounds__(256) void combine_uv_f32_kernel(CombineArgs a) {
+  constexpr int SL = 16;                       // 8 slices of 16 cover d_lat <= 128
   __shared__ float s_o[UV_M][UV_DLAT + 4];
   const int nmb = (a.batch * a.q_len + UV_M - 1) / UV_M;
   const int h = blockIdx.x / nmb;
@@ -206,21 +229,21 @@ __global__ __launch_bounds__(256) void combine_uv_f32_kernel(CombineArgs a) {
   {
     const int ml = threadIdx.x / 8, sl = threadIdx.x % 8;
     const int m = mb * UV_M + ml;
-    if (sl * SLICE < a.d_lat) {
-      float acc[SLICE];
+    if (sl * SL < a.d_lat) {
+      float acc[SL];
       float lse = -INFINITY;
       if (m < m_total) {
         const int b = m / a.q_len, j = m % a.q_len;
         const int jh = j * a.n_heads + h;
         int first, count;
         unit_slots(a, b, jh / kRowsPerWG, first, count);
-        lse = merge_slice(a, first, count, jh % kRowsPerWG, sl, acc);
+        lse = merge_slice<SL>(a, first, count, jh % kRowsPerWG, sl, acc);
       } else {
 #pragma unroll
-        for (int e = 0; e < SLICE; ++e) acc[e] = 0.f;
+        for (int e = 0; e < SL; ++e) acc[e] = 0.f;
       }
 #pragma unroll
-      for (int e = 0; e < SLICE; ++e) s_o[ml][sl * SLICE + e] = acc[e];
+      for (int e = 0; e < SL; ++e) s_o[ml][sl * SL + e] = acc[e];
       if (a.lse != nullptr && sl == 0 && m < m_total) a.lse[(int64_t)m * a.n_heads + h] = lse;
     }
   }
@@ -242,13 +265,16 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.batch * a.q_len * a.n_heads;
   if (rows == 0) return hipSuccess;
   if (a.w_uv == nullptr) {
-    hipLaunchKernelGGL(combine_latent_kernel, dim3((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG)),
-                       dim3(256), 0, s, a);
+    const dim3 grid((unsigned)((rows + ROWS_PER_WG - 1) / ROWS_PER_WG));
+    if (a.out_dtype == DT_BF16)
+      hipLaunchKernelGGL(combine_latent_kernel<32>, grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL(combine_latent_kernel<16>, grid, dim3(512), 0, s, a);
   } else {
     const int nmb = (a.batch * a.q_len + UV_M - 1) / UV_M;
     const unsigned grid = (unsigned)(nmb * a.n_heads);
     if (a.out_dtype == DT_BF16)
-      hipLaunchKernelGGL(combine_uv_bf16_kernel, dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(combine_uv_bf16_kernel, dim3(grid), dim3(512), 0, s, a);
     else
       hipLaunchKernelGGL(combine_uv_f32_kernel, dim3(grid), dim3(256), 0, s, a);
   }

@@ -29,6 +29,13 @@ def test_tiny_fp32_full():
     _run_check(inputs.workload(1))
 
 
+@pytest.mark.parametrize("d_c", [48, 112])
+def test_tiny_fp32_other_latent_widths(d_c):
+    """fp32 path at latent widths that are multiples of 16 but not of 32 or 64
+    (partial slices in the combine pass), two query tokens, ragged lengths."""
+    _run_check(inputs.workload(1, d_c=d_c, batch=3, q_len=2, seqlen=[256, 70, 2]))
+
+
 @pytest.mark.parametrize("seqlens", [[1], [65, 300, 31], [64, 128, 2, 5000]])
 def test_bf16_reduced_ragged(seqlens):
     """DeepSeek-V3 shapes, short and ragged lengths (tails inside a page, one token)."""
