@@ -30,10 +30,10 @@ __device__ __forceinline__ void unit_slots(const CombineArgs& a, int b, int rg, 
 
 // Merge the slice [W sl, W sl + W) of one row's partials (one thread).
 // Partials are bf16 when the activations are bf16 and f32 otherwise.  The
-// log-sum-exps of up to 8 splits, then the slices of up to 4 splits, are
-// loaded together before any arithmetic uses them.  Returns the row's
-// log-sum-exp (-inf: no visible key, acc = 0).
-constexpr int LSE_GROUP = 8;
+// splits are taken in groups of 4 whose log-sum-exps and slices are loaded
+// together, with a running maximum (the accumulated sum is rescaled when a
+// group raises it), so the merge waits for one round of loads per group.
+// Returns the row's log-sum-exp (-inf: no visible key, acc = 0).
 constexpr int PART_GROUP = 4;
 
 template <int W>
@@ -66,36 +66,38 @@ __device__ __forceinline__ float merge_slice(const CombineArgs& a, int first, in
                                              int sl, float (&acc)[W]) {
 #pragma unroll
   for (int e = 0; e < W; ++e) acc[e] = 0.f;
-  float mx = -INFINITY;
-  for (int s0 = 0; s0 < count; s0 += LSE_GROUP) {
-    float ls[LSE_GROUP];
-#pragma unroll
-    for (int s = 0; s < LSE_GROUP; ++s)
-      ls[s] = (s0 + s < count) ? a.part_lse[(int64_t)(first + s0 + s) * kRowsPerWG + r] : -INFINITY;
-#pragma unroll
-    for (int s = 0; s < LSE_GROUP; ++s) mx = fmaxf(mx, ls[s]);
-  }
-  if (mx == -INFINITY) return -INFINITY;
-  float tot = 0.f;
+  float mx = -INFINITY, tot = 0.f;
   for (int s0 = 0; s0 < count; s0 += PART_GROUP) {
-    float wgt[PART_GROUP];
+    float ls[PART_GROUP];
     float v[PART_GROUP][W];
 #pragma unroll
     for (int s = 0; s < PART_GROUP; ++s) {
       const bool in = s0 + s < count;
       const int64_t slot = first + (in ? s0 + s : 0);
-      const float ls = in ? a.part_lse[slot * kRowsPerWG + r] : -INFINITY;
+      ls[s] = in ? a.part_lse[slot * kRowsPerWG + r] : -INFINITY;
       load_slice<W>(a, slot, r, sl, v[s]);
-      // a split with no visible key (or past the count) weighs exactly 0
-      wgt[s] = ls == -INFINITY ? 0.f : __expf(ls - mx);
+    }
+    float gm = ls[0];
+#pragma unroll
+    for (int s = 1; s < PART_GROUP; ++s) gm = fmaxf(gm, ls[s]);
+    if (gm > mx) {
+      // a new maximum: rescale what has been summed so far (0 on the first group)
+      const float c = __expf(mx - gm);
+      tot *= c;
+#pragma unroll
+      for (int e = 0; e < W; ++e) acc[e] *= c;
+      mx = gm;
     }
 #pragma unroll
     for (int s = 0; s < PART_GROUP; ++s) {
-      tot += wgt[s];
+      // a split with no visible key (or past the count) weighs exactly 0
+      const float wgt = ls[s] == -INFINITY ? 0.f : __expf(ls[s] - mx);
+      tot += wgt;
 #pragma unroll
-      for (int e = 0; e < W; ++e) acc[e] += wgt[s] == 0.f ? 0.f : wgt[s] * v[s][e];
+      for (int e = 0; e < W; ++e) acc[e] += wgt == 0.f ? 0.f : wgt * v[s][e];
     }
   }
+  if (mx == -INFINITY) return -INFINITY;
   const float inv = 1.0f / tot;
 #pragma unroll
   for (int e = 0; e < W; ++e) acc[e] *= inv;
