@@ -39,8 +39,8 @@ __device__ __forceinline__ double rope_theta(int i, int d_rope, float base) {
 // bf16 (d_nope = 128, d_lat = 512): one workgroup per (head h, NB latent
 // columns, 64 rows m).  The W_UK[h] slice [128 x NB] bf16 is staged in LDS and
 // read as the A operand of D^T = W_UK[h]^T q^C^T with the LDS transpose read;
-// q^C rows are the B operand straight from global memory.  NB = 128 for bf16
-// output (4 column blocks per head, enough workgroups to cover the chip);
+// q^C rows are the B operand straight from global memory.  NB = 256 for bf16
+// output (2 column blocks per head: at 128 heads one workgroup per CU);
 // NB = 512 for e4m3 output, whose per-row scale max|q~| / 448 needs the whole
 // row in one workgroup.
 constexpr int AB_M = 64;
@@ -251,7 +251,7 @@ hipError_t launch_absorb_bf16(const AbsorbArgs& a, bool fp8_out, hipStream_t s) 
     hipLaunchKernelGGL((absorb_bf16_kernel<AB_N, true>), dim3((unsigned)(nmb * a.n_heads)),
                        dim3(256), 0, s, a);
   } else {
-    constexpr int NB = 128;
+    constexpr int NB = 256;
     hipLaunchKernelGGL((absorb_bf16_kernel<NB, false>),
                        dim3((unsigned)(nmb * a.n_heads * (AB_N / NB))), dim3(256), 0, s, a);
   }
