@@ -19,6 +19,9 @@ pages it follows:
 * [SLI]   "Deepseek-V3 Define 1: Higher Attachment of Head | by Shirley Li"
   (dataforcee.us), the multi-head-attention part, "Key Value Coverage" (the
   KV cache) and the rotary-embedding part ("Cords (rotating rotation").
+* "FP8 Mixed-Precision Training" (eeumee.net, the same tag page as [LKVC]),
+  section "Three Main Architectures" (RMSNorm of the compressed key/value in
+  FP32), for the cache append.
 * [SNAP]  "Related papers: SnapMLA: Efficient Long-Context MLA Decoding via H…"
   (scifaro.com), the abstract on two functionally equivalent kernel forms.
 
@@ -36,6 +39,8 @@ from .mla import (rope_theta, apply_rope, gather_cache, expand_kv,
                   absorb_query, mla_decode_expanded, mla_decode_absorbed,
                   decode_stored, DecodeResult, inputs_from_workload,
                   quantize_rows_e4m3)
+from .append import (rms_norm, append_positions, quantize_token_e4m3, append_kv,
+                     RMS_EPS)
 from .cache_sizes import (mla_cache_elems_per_token, mha_cache_elems_per_token,
                           gqa_cache_elems_per_token, mqa_cache_elems_per_token,
                           gqa_equivalent_groups)
@@ -45,6 +50,7 @@ __all__ = [
     "f64_to_e4m3_bits", "E4M3_MAX", "rope_theta", "apply_rope", "gather_cache",
     "expand_kv", "absorb_query", "mla_decode_expanded", "mla_decode_absorbed",
     "decode_stored", "DecodeResult", "inputs_from_workload", "quantize_rows_e4m3",
+    "rms_norm", "append_positions", "quantize_token_e4m3", "append_kv", "RMS_EPS",
     "mla_cache_elems_per_token",
     "mha_cache_elems_per_token", "gqa_cache_elems_per_token",
     "mqa_cache_elems_per_token", "gqa_equivalent_groups",
