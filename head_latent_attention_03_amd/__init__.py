@@ -9,11 +9,11 @@ marshalling for a decode batch, and the seeded synthetic workloads.
 """
 
 from ._binding import (LIBRARY_PATH, MLA_BF16, MLA_F32, MLA_FP8_E4M3, MlaDims, MlaError,
-                       load_library, mla_absorb_q, mla_combine, mla_decode_paged,
-                       mla_decode_workspace_size, mla_status_string)
+                       load_library, mla_absorb_q, mla_append_kv, mla_combine,
+                       mla_decode_paged, mla_decode_workspace_size, mla_status_string)
 
 __all__ = [
     "LIBRARY_PATH", "MLA_BF16", "MLA_F32", "MLA_FP8_E4M3", "MlaDims", "MlaError",
-    "load_library", "mla_absorb_q", "mla_combine", "mla_decode_paged",
+    "load_library", "mla_absorb_q", "mla_append_kv", "mla_combine", "mla_decode_paged",
     "mla_decode_workspace_size", "mla_status_string",
 ]

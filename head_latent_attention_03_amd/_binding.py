@@ -92,6 +92,9 @@ def load_library(path=LIBRARY_PATH):
     lib.mla_decode_paged.restype = ctypes.c_int
     lib.mla_combine.argtypes = [dp, i32, i32, _P, ctypes.c_size_t, _P, i32, _P, _P, _P, _P]
     lib.mla_combine.restype = ctypes.c_int
+    lib.mla_append_kv.argtypes = [dp, i32, i32, _P, _P, _P, ctypes.c_float, i32p, i32p, i32,
+                                  _P, _P, _P, i32, _P]
+    lib.mla_append_kv.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -208,3 +211,27 @@ def mla_combine(dims, workspace, seqlens, max_seqlen, w_uv, out, lse=None, q_len
         ctypes.byref(d), B, int(q_len), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _ptr(seqlens), int(max_seqlen),
         _ptr(w_uv), _ptr(out), _ptr(lse), _stream(stream)))
+
+
+def mla_append_kv(dims, kv_c, k_rope, norm_weight, norm_eps, seqlens, block_table, kv_latent,
+                  kv_scale, kv_rope, stream=None):
+    """Write the step's new tokens (RMSNorm'd latent, rotated k^R) into the paged cache;
+    see mla_append_kv in mla_decode.h."""
+    B, S = kv_c.shape[0], kv_c.shape[1]
+    dev = kv_c.device
+    act = dims.act_torch
+    P = kv_latent.shape[0]
+    _expect("kv_c", kv_c, (B, S, dims.d_latent), act, dev)
+    _expect("k_rope", k_rope, (B, S, dims.d_rope), act, dev)
+    _expect("norm_weight", norm_weight, (dims.d_latent,), act, dev)
+    _expect("seqlens", seqlens, (B,), torch.int32, dev)
+    _expect("block_table", block_table, (B, block_table.shape[1]), torch.int32, dev)
+    _expect("kv_latent", kv_latent, (P, dims.page_size, dims.d_latent), dims.latent_torch, dev)
+    if dims.latent_dtype == "e4m3":
+        _expect("kv_scale", kv_scale, (P, dims.page_size), torch.float32, dev)
+    _expect("kv_rope", kv_rope, (P, dims.page_size, dims.d_rope), act, dev)
+    d = dims.c()
+    _check("mla_append_kv", load_library().mla_append_kv(
+        ctypes.byref(d), B, S, _ptr(kv_c), _ptr(k_rope), _ptr(norm_weight), float(norm_eps),
+        _ptr(seqlens), _ptr(block_table), block_table.shape[1], _ptr(kv_latent),
+        _ptr(kv_scale), _ptr(kv_rope), P, _stream(stream)))

@@ -233,6 +233,50 @@ MLA_EXPORT mla_status_t mla_decode_paged(const mla_dims_t* dims, int32_t batch, 
   return launch_status(e);
 }
 
+MLA_EXPORT mla_status_t mla_append_kv(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                      const void* kv_c, const void* k_rope,
+                                      const void* norm_weight, float norm_eps,
+                                      const int32_t* seqlens, const int32_t* block_table,
+                                      int32_t max_pages_per_seq, void* kv_latent,
+                                      float* kv_scale, void* kv_rope, int32_t num_pages,
+                                      void* stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_batch(batch, q_len)) != MLA_OK) return st;
+  const bool fp8 = dims->latent_dtype == MLA_FP8_E4M3;
+  if (!kv_c || !k_rope || !norm_weight || !seqlens || !block_table || !kv_latent || !kv_rope)
+    return MLA_ERR_NULL_POINTER;
+  if (fp8 && !kv_scale) return MLA_ERR_NULL_POINTER;
+  if (!fp8 && kv_scale) return MLA_ERR_BAD_DTYPE;
+  if (num_pages < 1 || max_pages_per_seq < 1 || !(norm_eps > 0.f)) return MLA_ERR_BAD_SHAPE;
+  if (!aligned16(kv_c) || !aligned16(k_rope) || !aligned16(norm_weight) || !aligned16(seqlens) ||
+      !aligned16(block_table) || !aligned16(kv_latent) || !aligned16(kv_rope) ||
+      (fp8 && !aligned16(kv_scale)))
+    return MLA_ERR_MISALIGNED;
+  if (batch == 0) return MLA_OK;
+  mla::AppendArgs a;
+  a.kv_c = kv_c;
+  a.k_rope = k_rope;
+  a.norm_weight = norm_weight;
+  a.seqlens = seqlens;
+  a.block_table = block_table;
+  a.kv_lat = kv_latent;
+  a.kv_scale = kv_scale;
+  a.kv_rope = kv_rope;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.d_lat = dims->d_latent;
+  a.d_rope = dims->d_rope;
+  a.page_size = dims->page_size;
+  a.max_pages = max_pages_per_seq;
+  a.num_pages = num_pages;
+  a.act_dtype = dims->act_dtype;
+  a.lat_dtype = dims->latent_dtype;
+  a.eps = norm_eps;
+  a.rope_base = dims->rope_base;
+  return launch_status(mla::launch_append(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 MLA_EXPORT mla_status_t mla_combine(const mla_dims_t* dims, int32_t batch, int32_t q_len,
                                     const void* workspace, size_t workspace_bytes,
                                     const int32_t* seqlens, int32_t max_seqlen, const void* w_uv,

@@ -16,25 +16,6 @@
 namespace mla {
 namespace {
 
-// Rotation of one adjacent pair by pos * theta_i, theta_i = base^(-2i/d_rope).
-// The angle (up to ~6.5e4 rad) is formed and reduced to [-pi, pi] in fp64, so
-// the fp32 sin/cos that follow see a small argument; the rotation runs in
-// fp32.  theta is given in fp64.
-__device__ __forceinline__ void rope_pair(float x0, float x1, int pos, double theta, float& y0,
-                                          float& y1) {
-  constexpr double kTwoPi = 6.283185307179586476925286766559;
-  const double ang = (double)pos * theta;
-  const double red = ang - kTwoPi * rint(ang * (1.0 / kTwoPi));
-  float s, c;
-  sincosf((float)red, &s, &c);
-  y0 = x0 * c - x1 * s;
-  y1 = x0 * s + x1 * c;
-}
-
-__device__ __forceinline__ double rope_theta(int i, int d_rope, float base) {
-  return exp2(-2.0 * (double)i / (double)d_rope * log2((double)base));
-}
-
 // ---------------------------------------------------------------------------
 // bf16 (d_nope = 128, d_lat = 512): one workgroup per (head h, NB latent
 // columns, 64 rows m).  The W_UK[h] slice [128 x NB] bf16 is staged in LDS and

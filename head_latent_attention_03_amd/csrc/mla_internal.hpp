@@ -59,4 +59,21 @@ hipError_t launch_decode_fp8(const DecodeArgs& a, hipStream_t s, int grid);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s, int grid);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
+
+struct AppendArgs {
+  const void* kv_c;          // [batch, q_len, d_lat] act dtype, before RMSNorm
+  const void* k_rope;        // [batch, q_len, d_rope] act dtype, not rotated
+  const void* norm_weight;   // [d_lat] act dtype
+  const int32_t* seqlens;
+  const int32_t* block_table;
+  void* kv_lat;              // [num_pages, page_size, d_lat] latent dtype
+  float* kv_scale;           // [num_pages, page_size] (e4m3 latent only)
+  void* kv_rope;             // [num_pages, page_size, d_rope] act dtype
+  int32_t batch, q_len, d_lat, d_rope, page_size, max_pages, num_pages;
+  int32_t act_dtype, lat_dtype;  // Dt
+  float eps, rope_base;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
 }  // namespace mla

@@ -19,7 +19,8 @@
  * rotary-embedding part) and runs in FP32 ("Multi-Head Latent Attention –
  * Latent KV-Cache (DeepSeek v3)", eeumee.net, "FP8/FP32 Mixed Precision").
  *
- * One decode step is three calls on the caller's stream:
+ * One decode step is three calls on the caller's stream (after mla_append_kv
+ * has written the step's new tokens into the cache):
  *   mla_absorb_q      q~ = W_UK[h]^T q^C per head, and q_pe = RoPE(q^R) in fp32
  *   mla_decode_paged  split-KV attention of [q~; q_pe] over [c^KV; k^R] through
  *                     the block table; writes per-split partial results into
@@ -168,6 +169,42 @@ mla_status_t mla_combine(const mla_dims_t* dims, int32_t batch, int32_t q_len,
                          const void* workspace, size_t workspace_bytes,
                          const int32_t* seqlens, int32_t max_seqlen,
                          const void* w_uv, void* out, float* lse, void* stream);
+
+/*
+ * Append the new tokens of a decode step to the paged cache (run it before
+ * the step's mla_decode_paged).  New token j of sequence b sits at position
+ * pos = seqlens[b] - q_len + j (the lengths already count the new tokens);
+ * it is written at page block_table[b, pos / page_size], slot
+ * pos % page_size:
+ *   - latent: c = kv_c[b, j] / sqrt(mean(kv_c[b, j]^2) + norm_eps) * norm_weight,
+ *     computed in fp32 (RMSNorm of the compressed key/value in FP32: "FP8
+ *     Mixed-Precision Training", eeumee.net, "Three Main Architectures"),
+ *     stored in the latent dtype.  FP8_E4M3: kv_scale[row] = max|c| / 448
+ *     (1 for an all-zero row) and codes = e4m3(c / kv_scale[row]), rounded to
+ *     nearest-even, saturated at +-448 ("Multi-Head Latent Attention – Latent
+ *     KV-Cache (DeepSeek v3)", "FP8/FP32 Mixed Precision");
+ *   - rotary key: k_rope[b, j] with adjacent pairs rotated by
+ *     pos * rope_base^(-2i/d_rope) (angle in fp64, rotation in fp32), stored
+ *     in the act dtype: the decode reads k^R already rotated.
+ * A token with pos < 0 is not written.
+ *   kv_c        [batch, q_len, d_latent] act dtype, the latent before RMSNorm
+ *   k_rope      [batch, q_len, d_rope]   act dtype, not rotated
+ *   norm_weight [d_latent]               act dtype, the RMSNorm gain
+ *   norm_eps    > 0
+ *   seqlens, block_table, max_pages_per_seq, num_pages   as for mla_decode_paged
+ *   kv_latent, kv_scale (FP8_E4M3 latent only, else NULL), kv_rope: the cache,
+ *               modified in place at the new tokens' slots only
+ * Ownership and errors as for every call.  The same device preconditions
+ * apply; a table entry outside [0, num_pages) or a position past
+ * max_pages_per_seq * page_size is a broken precondition, for which the
+ * kernel writes nothing for that token.
+ */
+mla_status_t mla_append_kv(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                           const void* kv_c, const void* k_rope, const void* norm_weight,
+                           float norm_eps, const int32_t* seqlens,
+                           const int32_t* block_table, int32_t max_pages_per_seq,
+                           void* kv_latent, float* kv_scale, void* kv_rope,
+                           int32_t num_pages, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(mla_status_t status);
