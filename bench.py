@@ -157,8 +157,38 @@ def algorithmic(spec, seqlens):
     decode_f = 2 * H * vis * (spec.d_c + spec.d_rope) + 2 * H * vis * spec.d_c
     combine_b = H * spec.d_v * spec.d_c * a + rows * a * spec.d_v + rows * 4
     combine_f = 2 * rows * spec.d_c * spec.d_v
-    return {"absorb": (absorb_b, absorb_f), "decode": (decode_b, decode_f),
+    # append: read the new tokens' latent and rotary rows and the gain, write
+    # their cache rows (latent, rotary, e4m3 scale)
+    append_b = B * S * (a * (spec.d_c + spec.d_rope) + per_tok) + a * spec.d_c \
+        + seqlens.size * 4 + B * S * 4
+    return {"append": append_b, "absorb": (absorb_b, absorb_f), "decode": (decode_b, decode_f),
             "combine": (combine_b, combine_f), "tokens": tokens, "rows": rows}
+
+
+def append_time(spec, db, stream, steps):
+    """Average duration (us, HIP events) of mla_append_kv writing one new token
+    per query position of every sequence (the tokens at the end of the cache)."""
+    import torch
+    from head_latent_attention_03_amd import _binding as B
+    S, dev = spec.q_len, db.kv_latent.device
+    act = db.dims.act_torch
+    g = torch.Generator(device="cpu").manual_seed(31)
+    kv_c = torch.randn((spec.batch, S, spec.d_c), generator=g).to(act).to(dev)
+    k_r = torch.randn((spec.batch, S, spec.d_rope), generator=g).to(act).to(dev)
+    w = (1 + 0.1 * torch.randn((spec.d_c,), generator=g)).to(act).to(dev)
+    call = lambda: B.mla_append_kv(db.dims, kv_c, k_r, w, 1e-6, db.seqlens, db.block_table,
+                                   db.kv_latent, db.kv_scale, db.kv_rope, stream=stream)
+    for _ in range(5):
+        call()
+    n = max(10, min(steps, 100))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
 
 
 def cpu_baseline(wl, budget_s):
@@ -272,6 +302,10 @@ def main():
     ms_step = elapsed * 1e3 / args.steps
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev.values()]))
 
+    # the cache append of the step's new tokens (the step before decode, timed
+    # on its own after the main loop: it is not part of the metric's step)
+    app_us = append_time(spec, db, stream, args.steps)
+
     alg = algorithmic(spec, wl.seqlens)
     step_bytes = sum(v[0] for k, v in alg.items() if k in ("absorb", "decode", "combine"))
     step_flops = sum(v[1] for k, v in alg.items() if k in ("absorb", "decode", "combine"))
@@ -323,6 +357,14 @@ def main():
             "achieved_gbs": round(dec_b / (dec_ms * 1e-3) / 1e9, 2),
             "achieved_tflops": round(dec_f / (dec_ms * 1e-3) / 1e12, 2),
         },
+    }
+    app_b = alg["append"]
+    out["append"] = {
+        "kernel": "mla_append_kv", "us": round(app_us, 3), "tokens": spec.batch * spec.q_len,
+        "algorithmic_bytes": int(app_b),
+        "achieved_gbs": round(app_b / (app_us * 1e-6) / 1e9, 2),
+        "note": "one wave per new token; at this size the launch latency is the bound, "
+                "not HBM (the bytes would take well under 1 us at 8 TB/s)",
     }
     if args.cpu_budget > 0:
         t_cpu, frac, rows_done, threads = cpu_baseline(wl, args.cpu_budget)
