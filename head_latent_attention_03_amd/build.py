@@ -28,6 +28,13 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
+# per-source extra flags: the bf16 decode selects the VGPR form for the MFMAs
+# the compiler emits (the score accumulator is read by VALU code), while its
+# output accumulators are pinned to the accumulation registers by hand
+EXTRA_FLAGS = {
+    "decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _hipcc():
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
@@ -46,7 +53,8 @@ def sources():
 
 def _compile(hipcc, src, verbose):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
+    extra = EXTRA_FLAGS.get(os.path.basename(src), [])
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-I", CSRC, "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [hipcc, "-x", "hip", *cmd[1:]]
     res = subprocess.run(cmd, capture_output=True, text=True)

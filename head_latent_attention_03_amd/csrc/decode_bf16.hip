@@ -12,58 +12,54 @@
 // and the chunk's partial (o~ normalised by its own softmax sum, and its
 // natural-log log-sum-exp) for the combine pass.
 //
-// Mapping onto CDNA4 (8 waves, two per SIMD):
-//   * Scores: wave w owns rows 16w .. 16w+15; its absorbed query [16 x 576]
-//     bf16 stays in VGPRs.  Output: waves 2p and 2p+1 share rows 32p .. 32p+31
-//     and each accumulates half of the 512 latent columns for both row
-//     blocks ([32 x 256] f32 in registers), so every C^T block read from LDS
-//     feeds two MFMAs.  The pair swaps probabilities through LDS (1 KiB per
-//     wave and tile).  Per tile, LDS serves the score operand eight times
-//     (8 x 36 KiB) but the value operand four times (8 x 16 KiB), against
-//     eight times (8 x 32 KiB) when every wave holds whole rows.
-//   * The output product of tile i runs one iteration after its scores, so
-//     the probabilities a wave stores in iteration i are read by its partner
-//     in iteration i + 1, behind the one barrier every iteration has; they are
-//     double-buffered by tile parity.
+// Mapping onto CDNA4 (4 waves, one per SIMD, 512 registers each):
+//   * Wave w owns rows 32w .. 32w+31 outright: its absorbed query [32 x 576]
+//     bf16 (144 VGPRs) and its output accumulator [32 x 512] f32 (256
+//     registers, the accumulation file) stay resident for the whole chunk.
+//   * Both products use v_mfma_f32_32x32x16_bf16.  Against 16x16 blocks this
+//     halves the LDS bytes per flop of the operand that comes from LDS: a
+//     CU's four SIMDs at full MFMA rate then need 128 B/clk of LDS reads,
+//     where 16x16 blocks need 256 B/clk, more than the LDS delivers.
+//   * S^T = K Q^T: A = 32 K rows x 16 dims from LDS (one ds_read_b128 per
+//     lane), B = the query from registers.  The accumulator leaves lane l
+//     with head l & 31 and 16 tokens, 8(i >> 2) + 4(l >> 5) + (i & 3): the
+//     probabilities are already the B operand of the output product (lane =
+//     one head, 8 tokens per 16-token k-step), so they never touch LDS.
+//   * O^T += C^T P^T: A = 32 latent dims x 16 tokens, two ds_read_b64_tr_b16
+//     (the LDS transpose read) per lane, with the tokens in the order the
+//     score accumulator holds them.
+//   * The output product of tile i - 1 and the scores of tile i are issued
+//     alternately (independent accumulators), so the score chain's MFMA
+//     latency is hidden and the softmax of a tile overlaps nothing but its
+//     own tail.
 //   * The 32-token tile [c ; k^R] (32 x 1152 B) is brought from HBM straight
 //     into LDS with 16-byte global_load_lds (no VGPR staging), through a ring
 //     of 4 stages: iteration i reads stages i - 1 (output) and i (scores),
 //     tile i + 1 is in flight and tile i + 2 is copied into the stage that
-//     tile i - 2 released.  A sequence's page numbers sit one per lane in a
-//     VGPR and are read with v_readlane.
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16: A = K rows from LDS
-//     (ds_read_b128), B = the query from registers.  The accumulator leaves
-//     each lane with one head and 8 tokens, exactly the B operand of the
-//     output product, so the probabilities travel as one 16-byte chunk per
-//     lane.
-//   * O^T += C^T P^T with the same MFMA: A = C^T read with ds_read_b64_tr_b16
-//     (the LDS transpose read), B = P from LDS.
-//   * The HBM -> LDS copies are issued from inline asm (see dma16_s), so the
-//     compiler schedules the LDS reads freely; the ring is guarded by explicit
-//     vmcnt waits and one barrier per iteration.
+//     tile i - 2 released.  Each wave copies 8 latent rows and the 8 rotary
+//     rows of the same tokens per tile (9 instructions).  A sequence's page
+//     numbers sit one per lane in a VGPR and are read with v_readlane.
 //   * Online softmax in fp32 (base 2, scale folded).  Each row keeps a fixed
 //     reference maximum, set by its first scores, instead of rescaling the
 //     accumulator whenever the maximum grows: probabilities are
-//     exp2(s - m_ref) <= 2^64, so nothing overflows, and no cross-lane
-//     traffic is needed while scores stay below m_ref + 64.  If a score passes
-//     that, the workgroup runs its chunk once more with the true row maxima.
-//     The accumulator is thus only ever written by MFMAs, which is what lets
-//     two waves share a row's columns.
-//   * LDS rows are XOR-swizzled on 16-byte chunks so both read patterns are
-//     bank-conflict free on gfx950's LDS (64 banks of 4 bytes; a 16-byte read
-//     serves its 64 lanes in four 16-lane cycles, lanes taken in quads: the
-//     cycle of lane l is (l >> 5, parity of bits 2..4 of l); an 8-byte
-//     transpose read serves lanes 0-31, then 32-63).  Latent chunk c of token
-//     t sits at c ^ lat_key(t), lat_key(t) = 2(t & 7) ^ 9[bit 3 of t]:
-//       - QK: the 16 lanes of a cycle read chunk lg ^ lat_key(lr) for eight
-//         tokens with one lg and eight with lg ^ 1; the two key sets are
-//         unions of whole pairs {2m, 2m + 1} and fill all 16 chunk slots;
-//       - PV: the 8 tokens of a transpose half have distinct lat_key >> 1, so
-//         their 32-byte chunk pairs cover the 256-byte bank span once;
-//       - the copies: lat_key(4w + j) = lat_key(4w) ^ 2j, one XOR per row.
-//     Rotary chunk c sits at c ^ rope_key(t).  The probabilities are stored
-//     lane-major (chunk g of row h at g * 2 KiB + 16 h), so the 16 lanes of a
-//     cycle read 256 contiguous bytes.
+//     exp2(s - m_ref) <= 2^64, so nothing overflows and the accumulator is
+//     only ever written by MFMAs.  If a score passes m_ref + 64 the
+//     workgroup runs its chunk once more with the true row maxima.
+//   * LDS rows are XOR-swizzled on 16-byte chunks so that both read patterns
+//     are bank-conflict free on gfx950's LDS (64 banks of 4 bytes; a 16-byte
+//     read serves its 64 lanes in four 16-lane cycles, lanes taken in quads:
+//     the cycle of lane l is (l >> 5, parity of bits 2..4 of l); an 8-byte
+//     transpose read serves lanes 0-31, then 32-63).  Latent chunk c of
+//     token t sits at slot (c & 15) ^ lat_key(t) of its 256-byte group c >> 4,
+//     lat_key(t) = 4(t & 3) + ((t >> 2) & 3):
+//       - QK: a cycle's 16 lanes read one chunk of 16 tokens 4a + r whose a
+//         share a parity; (r, a & 3) takes each of its 16 values once;
+//       - PV: a transpose half reads 4 consecutive chunks of 4 consecutive
+//         tokens; 4(t & 3) spreads the tokens over the high two slot bits
+//         while the chunks fill the low two.
+//     Rotary chunk c (0..7) of token t sits at c ^ rope_key(t), rope_key(t)
+//     = ((t >> 2) & 3) + 4((t >> 1) & 1); with the row's 128-byte offset
+//     (bit 0 of t) it separates the 16 tokens of a QK cycle.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -74,55 +70,70 @@ constexpr int D_LAT = 512;
 constexpr int D_ROPE = 64;
 constexpr int LAT_ROW = D_LAT * 2;         // bytes per cached latent row
 constexpr int ROPE_ROW = D_ROPE * 2;       // bytes per cached rotary row
-constexpr int KS_LAT = D_LAT / 32;         // QK k-steps over the latent
-constexpr int KS_ROPE = D_ROPE / 32;       // QK k-steps over the rotary part
-constexpr int KS = KS_LAT + KS_ROPE;
-constexpr int DB = D_LAT / 16;             // 16-column output blocks
-constexpr int DBH = DB / 2;                // output column blocks per wave
-constexpr int LAT_STAGE = kTile * LAT_ROW;   // 32 KiB
+constexpr int KS_LAT = D_LAT / 16;         // QK k-steps over the latent
+constexpr int KS_ROPE = D_ROPE / 16;       // QK k-steps over the rotary part
+constexpr int KS = KS_LAT + KS_ROPE;       // 36
+constexpr int DB = D_LAT / 32;             // 32-dim output blocks
+constexpr int PV_STEPS = 2 * DB;           // two 16-token k-steps per tile
+constexpr int LAT_PITCH = LAT_ROW + 64;      // LDS pitch of a latent row
+constexpr int LAT_STAGE = kTile * LAT_PITCH; // 34 KiB
 constexpr int ROPE_STAGE = kTile * ROPE_ROW; // 4 KiB
 constexpr int STAGE = LAT_STAGE + ROPE_STAGE;
 constexpr int NSTAGE = 4;
 constexpr float kRefSlack = 64.0f;         // log2 units
 
-constexpr int kWaves = kRowsPerWG / 16;    // 8
-constexpr int kThreads = 64 * kWaves;
-constexpr int kLatRows = kTile / kWaves;   // latent rows each wave copies per tile (4)
+constexpr int NW = kRowsPerWG / 32;        // 4 waves
+constexpr int kThreads = 64 * NW;
+constexpr int kLatRows = kTile / NW;       // latent rows each wave copies per tile (8)
 constexpr int kDma = kLatRows + 1;         // copies per wave per tile
-constexpr int P_BUF = kRowsPerWG * kTile * 2;  // one tile's probabilities, bf16 (8 KiB)
-constexpr int P_CHUNK = kRowsPerWG * 16;       // bytes per 16-byte chunk column (2 KiB)
+constexpr int kDmaEvery = 4;               // MFMA steps between a wave's copies
 
-// the ring and the two probability buffers fill the 160 KiB of LDS exactly;
-// the few words needed after a pass (the second-pass flags, 1 / l) reuse the
-// probability buffers once the pass is over
 __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NSTAGE * STAGE];
-__shared__ __attribute__((aligned(1024))) uint8_t s_p[2 * P_BUF];
-static_assert(NSTAGE * STAGE + 2 * P_BUF <= 160 * 1024, "LDS budget");
+__shared__ int s_flag[NW];
+static_assert(NSTAGE * STAGE + NW * 4 <= 160 * 1024, "LDS budget");
 
-// swizzle keys (see the header); both depend on t & 15 only
-__device__ __forceinline__ int lat_key(int t) { return ((t & 7) << 1) ^ (((t >> 3) & 1) * 9); }
-__device__ __forceinline__ int rope_key(int t) { return (t >> 1) & 7; }
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__device__ __forceinline__ f32x16 mfma32(u16x8 a, u16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// acc += A B with the accumulator pinned to the accumulation registers.  The
+// 256 of them hold exactly the wave's output [32 x 512]; left to itself the
+// allocator also places the score accumulator there and then moves an output
+// block between register files every tile.  Each output block is updated by
+// MFMAs only, at least 15 MFMAs apart; mfma_drain() covers the MFMA latency
+// before anything else reads or writes the accumulators.
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, u16x8 a, u16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
+
+// LDS byte offset of latent row t within a stage, and the rotary swizzle key
+// (see the header)
+__host__ __device__ constexpr int lat_row(int t) { return t * LAT_PITCH + 16 * ((t >> 2) & 3); }
+__device__ __forceinline__ int rope_key(int t) { return ((t >> 2) & 3) | (((t >> 1) & 1) << 2); }
+static_assert(lat_row(kTile - 1) + LAT_ROW <= LAT_STAGE, "latent rows fit the stage");
 
 __device__ __forceinline__ MLA_LDS uint8_t* stage_base(int st) {
   return (MLA_LDS uint8_t*)s_ring + st * STAGE;
 }
 
-// The copies of one tile: this wave's kLatRows latent rows (parts
-// 0..kLatRows-1) and the rotary rows of the same tokens (last part, on half
-// the lanes).  Tokens past the end of the sequence re-read its last token
-// (finite data that the mask then ignores), so every wave issues the same
-// count.  The parts are issued along a phase's MFMA steps, so their issue
-// (which waits while the memory pipeline is full) overlaps the MFMAs.
+// The copies of one tile: wave w's latent rows 8w .. 8w+7 (parts 0..7, one
+// 1 KiB row each) and the rotary rows of the same tokens (part 8).  Tokens
+// past the end of the sequence re-read its last token (finite data that the
+// mask then ignores), so every wave issues the same count.
 struct TileCopy {
   const uint8_t* lat;    // first latent row of the tile
   const uint8_t* rope;   // first rotary row of the tile
   int tok0, last;        // first token of the tile, last token of the sequence
   int st;                // ring stage
-  bool valid;
 };
 
 __device__ __forceinline__ TileCopy tile_copy(const DecodeArgs& a, int page, int len, int k,
-                                              int st, bool valid) {
+                                              int st) {
   TileCopy c;
   c.tok0 = k * kTile;
   c.last = len - 1;
@@ -130,27 +141,22 @@ __device__ __forceinline__ TileCopy tile_copy(const DecodeArgs& a, int page, int
   c.lat = (const uint8_t*)a.kv_lat + row0 * LAT_ROW;
   c.rope = (const uint8_t*)a.kv_rope + row0 * ROPE_ROW;
   c.st = st;
-  c.valid = valid;
   return c;
 }
 
 __device__ __forceinline__ void issue_part(const TileCopy& c, int j, int w, int lane) {
-  constexpr int NL = kLatRows;
-  static_assert(NL * ROPE_ROW * 2 == 1024, "a wave's rotary rows fill half a 1 KiB copy");
+  static_assert(kLatRows * ROPE_ROW == 1024, "a wave's rotary rows fill one 1 KiB copy");
   MLA_LDS uint8_t* dst = stage_base(c.st);
-  if (j < NL) {
-    // lat_key(w*NL + q) = lat_key(w*NL) ^ 2q for q < NL, so the source chunk
-    // offsets of the wave's rows are one per-lane value XOR 32q
-    uint32_t off0 = (uint32_t)((lane ^ lat_key(w * NL)) << 4);
-    asm volatile("" : "+v"(off0));
-    const int t = w * NL + j;
+  if (j < kLatRows) {
+    // one row, copied as it is: lane l brings chunk l
+    const int t = w * kLatRows + j;
     const int tc = min(c.tok0 + t, c.last) - c.tok0;
-    dma16_s(c.lat + tc * LAT_ROW, off0 ^ (uint32_t)(j << 5), dst + t * LAT_ROW);
+    dma16_s(c.lat + tc * LAT_ROW, (uint32_t)(lane << 4), dst + lat_row(t));
   } else {
-    const int t = w * NL + (lane >> 3);
+    const int t = w * kLatRows + (lane >> 3);
     const int tc = min(c.tok0 + t, c.last) - c.tok0;
     const uint32_t off = (uint32_t)(tc * ROPE_ROW + (((lane & 7) ^ rope_key(t)) << 4));
-    if (lane < NL * 8) dma16_s(c.rope, off, dst + LAT_STAGE + w * NL * ROPE_ROW);
+    dma16_s(c.rope, off, dst + LAT_STAGE + w * kLatRows * ROPE_ROW);
   }
 }
 
@@ -171,309 +177,274 @@ __device__ __forceinline__ void barrier() {
 
 struct State {
   u16x8 q[KS];          // absorbed query of the wave's rows (B operand)
-  f32x4 o[2][DBH];      // O^T accumulator of the pair's row block j and this
-                        // wave's column block: lane holds head lr, 4 latent dims
+  f32x16 o[DB];         // O^T accumulator: lane holds head l & 31 and 16 of
+                        // the block's 32 latent dims
   float m, l;           // reference max (log2 units, scaled) and per-lane sum
   int lim;              // keys visible to the lane's row: t < lim
   float tmax;           // largest score this lane has seen (log2 units, scaled)
   bool redo;            // a score passed m_ref + 64 with mass already accumulated
 };
 
-// Per-lane LDS byte offsets of the read patterns (from a stage's base, or
-// from a probability buffer).  Every address a tile reads is one of them
-// XOR or plus a small constant:
-//   QK latent, chunk group v:  qk ^ (v << 6)   ((v*4 + lg) ^ key = (lg ^ key) ^ 4v)
-//   QK rotary, chunk group v:  rp ^ (v << 6)
-//   PV transpose, column db:   pv ^ ((db & 7) << 5), + 256 per 8 columns
-//   probabilities of block rb: p + 256 rb
-// (the bases are 1 KiB aligned and the XORed bits never carry).
+// Per-lane LDS byte offsets of the read patterns (from a stage's base).  The
+// latent reads are one of them plus an immediate:
+//   QK latent, k-step ks:   qk + 32 ks
+//   QK rotary, k-step 32+k: rp ^ (2k << 4)
+//   PV block db, k-step kb, read r (tokens +8r):
+//                           pv + LAT_PITCH (16kb + 8r) + 32r + 64db
+// (lat_row(t0 + t) = lat_row(t) + LAT_PITCH t0 + 32 (t0 >> 3 & 1) for t0 a
+// multiple of 8 and t < 8).
 struct LaneOff {
-  uint32_t qk, rp, pv, p;
+  uint32_t qk, rp, pv;
 };
 
 __device__ __forceinline__ LaneOff lane_offsets(int lane) {
-  const int lr = lane & 15, lg = lane >> 4;
-  const int t1 = lg * 4 + (lr >> 2);
+  const int lc = lane & 31, hh = lane >> 5;
+  const int dh = (lane >> 4) & 1, lr = lane & 15;
   LaneOff o;
-  o.qk = (uint32_t)(lr * LAT_ROW + ((lg ^ lat_key(lr)) << 4));
-  o.rp = (uint32_t)(LAT_STAGE + lr * ROPE_ROW + ((lg ^ rope_key(lr)) << 4));
-  o.pv = (uint32_t)(t1 * LAT_ROW + ((((lr & 3) >> 1) ^ lat_key(t1)) << 4) + ((lr & 1) << 3));
-  o.p = (uint32_t)(lg * P_CHUNK + lr * 16);
+  // QK: lane reads token lc, chunk 2ks + hh
+  o.qk = (uint32_t)(lat_row(lc) + 16 * hh);
+  o.rp = (uint32_t)(LAT_STAGE + lc * ROPE_ROW + ((hh ^ rope_key(lc)) << 4));
+  // PV transpose read: lane addresses token 4hh + (lr >> 2) (+16kb + 8r) and
+  // latent dims 32db + 16dh + 4(lr & 3) .. +3: chunk 4db + 2dh + ((lr & 3) >> 1),
+  // byte 8 (lr & 1)
+  o.pv = (uint32_t)(lat_row(4 * hh + (lr >> 2)) + 16 * (2 * dh + ((lr & 3) >> 1)) + 8 * (lr & 1));
   return o;
 }
 
-// ---- S^T[t, h] = K[t, :] . Q[h, :] for one tile (t = tb*16 + row of the
-// 16x16 block).  Also issues the copy parts of a later tile (cp), one per two
-// k-steps.
-__device__ __forceinline__ void tile_qk(const State& S, int st, int lane, LaneOff lo,
-                                        const TileCopy& cp, int w, f32x4 (&sacc)[2]) {
-  static_assert(2 * kDma <= KS, "a tile's copies fit in the QK k-steps");
-  const MLA_LDS uint8_t* lat = stage_base(st);
-  asm volatile("" : "+v"(lo.qk), "+v"(lo.rp));
-  sacc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-  sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // latent chunk kk*4 + lg of token tb*16 + lr sits at ((kk & 3)*4 + lg) ^ key
-  // within the 16-chunk group kk >> 2 (key < 16); rotary chunk k2*4 + lg at
-  // (k2*4 + lg) ^ rope_key
-  auto load_k = [&](int kk, int tb) -> u16x8 {
-    if (kk < KS_LAT)
-      return *(const MLA_LDS u16x8*)(lat + (lo.qk ^ (uint32_t)((kk & 3) << 6)) + tb * 16 * LAT_ROW +
-                                     (kk >> 2) * 256);
-    return *(const MLA_LDS u16x8*)(lat + (lo.rp ^ (uint32_t)((kk - KS_LAT) << 6)) +
-                                   tb * 16 * ROPE_ROW);
-  };
-  // A operands are read QK_AHEAD k-steps ahead of their MFMAs
-#ifdef MLA_QK_AHEAD
-  constexpr int QK_AHEAD = MLA_QK_AHEAD;
+// A operand of score k-step ks (K rows of tile stage kq), and of output step
+// j: k-step kb = j >> 4 (tokens 16kb ..), block db = j & 15 (C^T of stage kv)
+__device__ __forceinline__ u16x8 load_k(const MLA_LDS uint8_t* kq, const LaneOff& lo, int ks) {
+  if (ks < KS_LAT) return *(const MLA_LDS u16x8*)(kq + lo.qk + 32 * ks);
+  return *(const MLA_LDS u16x8*)(kq + (lo.rp ^ (uint32_t)((2 * (ks - KS_LAT)) << 4)));
+}
+
+__device__ __forceinline__ u16x8 load_v(const MLA_LDS uint8_t* kv, const LaneOff& lo, int j) {
+  const int kb = j >> 4, db = j & 15;
+  const MLA_LDS uint8_t* b = kv + lo.pv + 16 * kb * LAT_PITCH + 64 * db;
+  const u16x4 lo4 = lds_read_tr16(b);
+  const u16x4 hi4 = lds_read_tr16(b + 8 * LAT_PITCH + 32);
+  return u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+}
+
+// LDS reads run this many MFMA steps ahead of their use
+#ifdef MLA_AHEAD
+constexpr int AH = MLA_AHEAD;
 #else
-  constexpr int QK_AHEAD = 2;
+constexpr int AH = 2;
 #endif
-  u16x8 ka[QK_AHEAD][2];
+
+// One pipeline step group: the scores of tile stage st_qk (if QK) and the
+// output product of tile stage st_pv with probabilities p (if PV), issued
+// alternately, plus the copies of a later tile (cp), one every kDmaEvery
+// steps.  A copy instruction holds its wave for some 50 cycles; issued ahead
+// of a step's MFMAs, part of that hides behind the MFMA still running.
+template <bool QK, bool PV, bool COPY, int PHASE = 0>
+__device__ __forceinline__ void tile_step(State& S, int st_qk, int st_pv, const u16x8 (&p)[2],
+                                          int lane, LaneOff lo, const TileCopy& cp, int w,
+                                          f32x16& sacc) {
+  constexpr int NSTEP = QK ? KS : PV_STEPS;
+  static_assert(kDmaEvery * (kDma - 1) + kDmaEvery - 1 < KS, "a tile's copies fit in the score steps");
+  const MLA_LDS uint8_t* kq = stage_base(st_qk);
+  const MLA_LDS uint8_t* kv = stage_base(st_pv);
+  asm volatile("" : "+v"(lo.qk), "+v"(lo.rp), "+v"(lo.pv));
+  u16x8 ka[AH], va[AH];
+  if (QK) sacc = f32x16{};
 #pragma unroll
-  for (int j = 0; j < QK_AHEAD; ++j) {
-    ka[j][0] = load_k(j, 0);
-    ka[j][1] = load_k(j, 1);
+  for (int j = 0; j < AH; ++j) {
+    if (QK) ka[j] = load_k(kq, lo, j);
+    if (PV) va[j] = load_v(kv, lo, j);
   }
 #pragma unroll
-  for (int kk = 0; kk < KS; ++kk) {
-    const u16x8 cur0 = ka[kk % QK_AHEAD][0], cur1 = ka[kk % QK_AHEAD][1];
-    if (kk + QK_AHEAD < KS) {
-      ka[kk % QK_AHEAD][0] = load_k(kk + QK_AHEAD, 0);
-      ka[kk % QK_AHEAD][1] = load_k(kk + QK_AHEAD, 1);
+  for (int j = 0; j < NSTEP; ++j) {
+    // a copy is issued while the previous step's MFMA still runs
+    if (COPY && j % kDmaEvery == PHASE && j / kDmaEvery < kDma)
+      issue_part(cp, j / kDmaEvery, w, lane);
+    if (QK) {
+      const u16x8 cur = ka[j % AH];
+      if (j + AH < KS) ka[j % AH] = load_k(kq, lo, j + AH);
+      sacc = mfma32(cur, S.q[j], sacc);
     }
-    sacc[0] = mfma_bf16_16x16x32(cur0, S.q[kk], sacc[0]);
-    sacc[1] = mfma_bf16_16x16x32(cur1, S.q[kk], sacc[1]);
-    if ((kk & 1) == 0 && (kk >> 1) < kDma && cp.valid) issue_part(cp, kk >> 1, w, lane);
+    if (PV && j < PV_STEPS) {
+      const u16x8 cur = va[j % AH];
+      if (j + AH < PV_STEPS) va[j % AH] = load_v(kv, lo, j + AH);
+      mfma32_acc(S.o[j & (DB - 1)], cur, p[j >> 4]);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// One probability: the lane's score r of token block tb, masked, in log2
-// units relative to the row's reference m; tracks the lane's largest score
-// and whether any passed m + 64.
-__device__ __forceinline__ float tile_prob(const DecodeArgs& a, State& S, const f32x4 (&sacc)[2],
-                                           int tok0, int lg, int tb, int r, bool& need) {
-  const int t = tok0 + tb * 16 + lg * 4 + r;
-  const float v = (t < S.lim) ? sacc[tb][r] * a.scale_log2 : -INFINITY;
-  S.tmax = fmaxf(S.tmax, v);
-  need |= v > S.m + kRefSlack;
-  // (the clamp only matters in a pass that will be redone)
-  return (S.m == -INFINITY) ? 0.f : fast_exp2(fminf(v - S.m, kRefSlack));
+// The probabilities of the later tiles packed as bf16 pairs (see above); with
+// MASK, keys at or past the row's limit are cut.
+template <bool MASK>
+__device__ __forceinline__ void later_probs(const DecodeArgs& a, State& S, const f32x16& sacc,
+                                            int tok0, int hh, uint32_t (&pk)[8]) {
+  const float m_eff = S.m == -INFINITY ? INFINITY : S.m;
+  float d[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) d[i] = fmaf(sacc[i], a.scale_log2, -m_eff);
+  if (MASK && __ballot(tok0 + kTile > S.lim)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (tok0 + 8 * (i >> 2) + 4 * hh + (i & 3) >= S.lim) d[i] = -INFINITY;
+  }
+  float dmx = d[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) dmx = fmaxf(dmx, d[i]);
+  // (a row without reference gives -inf + inf = NaN, which fmaxf ignores)
+  S.tmax = fmaxf(S.tmax, dmx + m_eff);
+  S.redo |= dmx > kRefSlack;
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+    pk[c] = pack_bf16x2(fast_exp2(fminf(d[2 * c], kRefSlack)),
+                        fast_exp2(fminf(d[2 * c + 1], kRefSlack)));
 }
 
-// Online softmax of one tile; lane holds head lr, tokens tb*16 + lg*4 + r.
-// Returns the probabilities packed as the B operand (bf16) and adds their
-// rounded values to the lane's sum.
-//   * The chunk's first tile (first): a row's first scores set its
-//     reference, formed across the row's four lanes; a jump past the
-//     reference + 64 marks the workgroup for a second pass.
-//   * Later tiles: every row with a visible key in the chunk has its
-//     reference (the first tile holds the chunk's first key, and visibility
-//     is a prefix), so d = s - m is one FMA per score, the jump test is one
-//     compare per tile and masking is needed only on a tile that crosses
-//     some row's limit.  A row with no reference has no visible key: its
-//     d is -inf (m taken as +inf).
-__device__ __forceinline__ u16x8 tile_softmax(const DecodeArgs& a, State& S,
-                                              const f32x4 (&sacc)[2], int tok0, int lane,
-                                              bool first) {
-  const int lg = lane >> 4;
-  uint32_t pk[4];
-  float psum = 0.f;
+// Adds the rounded probabilities to the lane's sum (v_dot2 with ones, so the
+// sum sees the values the MFMA multiplies) and forms the two B operands.
+__device__ __forceinline__ void finish_probs(State& S, const uint32_t (&pk)[8], u16x8 (&pout)[2]) {
   const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  if (first) {
-    float mx = -INFINITY;
+  float psum = 0.f;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tok0 + tb * 16 + lg * 4 + r;
-        mx = fmaxf(mx, (t < S.lim) ? sacc[tb][r] * a.scale_log2 : -INFINITY);
-      }
-    if (__ballot(mx > S.m + kRefSlack)) {
-      mx = wave_max_xor(mx, 16);
-      mx = wave_max_xor(mx, 32);
-      float mass = S.l;
-      mass = wave_sum_xor(mass, 16);
-      mass = wave_sum_xor(mass, 32);
-      if (mx > S.m + kRefSlack && mass == 0.f) S.m = mx;
-    }
-    bool need = false;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const float p0 = tile_prob(a, S, sacc, tok0, lg, tb, r, need);
-        const float p1 = tile_prob(a, S, sacc, tok0, lg, tb, r + 1, need);
-        pk[tb * 2 + r / 2] = pack_bf16x2(p0, p1);
-      }
-    S.redo |= need;
-  } else {
-    const float m_eff = S.m == -INFINITY ? INFINITY : S.m;
-    float d[2][4];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) d[tb][r] = fmaf(sacc[tb][r], a.scale_log2, -m_eff);
-    if (__ballot(tok0 + kTile > S.lim)) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (tok0 + tb * 16 + lg * 4 + r >= S.lim) d[tb][r] = -INFINITY;
-    }
-    const float dmx = fmaxf(fmaxf(fmaxf(d[0][0], d[0][1]), fmaxf(d[0][2], d[0][3])),
-                            fmaxf(fmaxf(d[1][0], d[1][1]), fmaxf(d[1][2], d[1][3])));
-    // (a row without reference gives -inf + inf = NaN, which fmaxf ignores)
-    S.tmax = fmaxf(S.tmax, dmx + m_eff);
-    S.redo |= dmx > kRefSlack;
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int r = 0; r < 4; r += 2)
-        pk[tb * 2 + r / 2] = pack_bf16x2(fast_exp2(fminf(d[tb][r], kRefSlack)),
-                                         fast_exp2(fminf(d[tb][r + 1], kRefSlack)));
-  }
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
+  for (int c = 0; c < 8; ++c)
     psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[c]), one2, psum, false);
   S.l += psum;
-  return __builtin_bit_cast(u16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+  pout[0] = __builtin_bit_cast(u16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+  pout[1] = __builtin_bit_cast(u16x8, u32x4{pk[4], pk[5], pk[6], pk[7]});
 }
 
-// ---- O^T[d, h] += C^T[d, t] P^T[t, h] for the pair's two row blocks and
-// this wave's 16 column blocks of tile stage st, probabilities from buffer
-// par.  Also issues the copy parts of a later tile (cp).
-__device__ __forceinline__ void tile_pv(State& S, int st, int par, int lane, LaneOff lo,
-                                        const TileCopy& cp, int w) {
-  static_assert(3 * (kDma - 1) < DBH, "a tile's copies fit in the PV steps");
-  const int pr = w >> 1, half = w & 1;
-  // the wave's columns start at chunk group half * 2 of each latent row
-  const MLA_LDS uint8_t* lat = stage_base(st) + half * 512;
-  const MLA_LDS uint8_t* pb = (const MLA_LDS uint8_t*)s_p + par * P_BUF + pr * 2 * 256;
-  asm volatile("" : "+v"(lo.pv), "+v"(lo.p));
-  const u16x8 p0 = *(const MLA_LDS u16x8*)(pb + lo.p);
-  const u16x8 p1 = *(const MLA_LDS u16x8*)(pb + lo.p + 256);
-  // transpose read: lane (lg, lr) addresses token row lg*4 + lr/4 (and +16),
-  // latent dims db*16 + (lr&3)*4 .. +3, i.e. chunk 2db + (lr&3)/2, which sits
-  // at ((2(db & 7) + (lr&3)/2) ^ key) in chunk group db >> 3
-  auto load_c = [&](int db) -> u16x8 {
-    const MLA_LDS uint8_t* p = lat + (lo.pv ^ (uint32_t)((db & 7) << 5)) + (db >> 3) * 256;
-    const u16x4 lo4 = lds_read_tr16(p);
-    const u16x4 hi4 = lds_read_tr16(p + 16 * LAT_ROW);
-    return u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-  };
-#ifdef MLA_PV_AHEAD
-  constexpr int PV_AHEAD = MLA_PV_AHEAD;
-#else
-  constexpr int PV_AHEAD = 2;
-#endif
-  u16x8 ca[PV_AHEAD];
+// Online softmax of a tile, in two parts.  Lane holds head l & 31 and tokens
+// 8(i >> 2) + 4hh + (i & 3) of the tile.
+//   * set_reference (the chunk's first tile only): a row's first scores set
+//     its reference, formed across the row's two lanes.
+//   * probs: every row with a visible key in the chunk has its reference by
+//     then (the first tile holds the chunk's first key, and visibility is a
+//     prefix), so d = s - m is one FMA per score, a jump past the reference
+//     + 64 is one compare per tile (it marks the workgroup for a second
+//     pass), and masking is needed only on a tile that crosses some row's
+//     limit.  A row with no reference has no visible key: its d is -inf (m
+//     taken as +inf).
+__device__ __forceinline__ void set_reference(const DecodeArgs& a, State& S, const f32x16& sacc,
+                                              int tok0, int lane) {
+  const int hh = lane >> 5;
+  float mx = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < PV_AHEAD; ++j) ca[j] = load_c(j);
-#pragma unroll
-  for (int db = 0; db < DBH; ++db) {
-    const u16x8 av = ca[db % PV_AHEAD];
-    if (db + PV_AHEAD < DBH) ca[db % PV_AHEAD] = load_c(db + PV_AHEAD);
-    S.o[0][db] = mfma_bf16_16x16x32(av, p0, S.o[0][db]);
-    S.o[1][db] = mfma_bf16_16x16x32(av, p1, S.o[1][db]);
-    if (db % 3 == 0 && db / 3 < kDma && cp.valid) issue_part(cp, db / 3, w, lane);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int i = 0; i < 16; ++i) {
+    const int t = tok0 + 8 * (i >> 2) + 4 * hh + (i & 3);
+    mx = fmaxf(mx, (t < S.lim) ? sacc[i] * a.scale_log2 : -INFINITY);
+  }
+  if (__ballot(mx > S.m + kRefSlack)) {
+    mx = wave_max_xor(mx, 32);
+    const float mass = wave_sum_xor(S.l, 32);
+    if (mx > S.m + kRefSlack && mass == 0.f) S.m = mx;
   }
 }
+
+template <bool MASK>
+__device__ __forceinline__ void probs(const DecodeArgs& a, State& S, const f32x16& sacc, int tok0,
+                                      int lane, u16x8 (&pout)[2]) {
+  uint32_t pk[8];
+  later_probs<MASK>(a, S, sacc, tok0, lane >> 5, pk);
+  finish_probs(S, pk, pout);
+}
+
 
 // One pass over the chunk's tiles [k0, k0 + n).  Iteration i (0 <= i <= n)
 // runs the output product of tile i - 1 and the scores of tile i.
-template <typename AfterFirst>
+// The pass starts by copying tiles 0 and 1 and calling `loads`, which issues
+// NLOADS vector loads (the query, on the first pass).  Tile 0 is waited for
+// alone; the compiler waits for each loaded register where the first scores
+// use it, so those start before the loads have all landed.  Tile 2 is copied
+// after them: a copy issued earlier would sit among the loads the compiler
+// counts and hold up those waits.
+template <int NLOADS, typename Loads>
 __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Chunk& ch, int k0,
-                                         int n, int w, int lane, AfterFirst after_first) {
-  constexpr int D = kDma;
+                                         int n, int w, int lane, Loads loads) {
   const LaneOff lo = lane_offsets(lane);
   const int32_t* bt_row = a.block_table + (int64_t)ch.b * a.max_pages;
   PageWindow W;
   W.pg0 = uni(k0 * kTile / kPage);
   W.v = page_window_load(bt_row, a.max_pages, W.pg0, lane);
-  auto copy_of = [&](int k, int st, bool valid) {
-    const int page = valid ? page_lookup(W, bt_row, a.max_pages, k * kTile / kPage, lane) : 0;
-    return tile_copy(a, page, ch.len, k, st, valid);
+  // every iteration copies one tile, so that the copy count (and with it each
+  // vmcnt wait) is the same on every path; a copy past the chunk's last tile
+  // re-reads that tile into a stage that is not read again
+  const int k_last = k0 + n - 1;
+  auto copy_of = [&](int k, int st) {
+    k = min(k, k_last);
+    const int page = page_lookup(W, bt_row, a.max_pages, k * kTile / kPage, lane);
+    return tile_copy(a, page, ch.len, k, st);
   };
-  // tile 0 first (with whatever the caller loads next); tile 1 once it has
-  // landed, so that the first wait is not behind it
-  issue_tile(copy_of(k0, 0, true), w, lane);
-  after_first();
-  // tile 0 and the caller's loads have landed; the query registers are
-  // marked used here so that the compiler's own wait for them falls at this
-  // point (where it is free) and not after the next copies are in flight
-  wait_vm<0>();
-#pragma unroll
-  for (int kk = 0; kk < KS; ++kk) asm volatile("" ::"v"(S.q[kk]));
+  issue_tile(copy_of(k0, 0), w, lane);
+  issue_tile(copy_of(k0 + 1, 1), w, lane);
+  loads();
+  wait_vm<kDma + NLOADS>();
   barrier();
-  if (n > 1) issue_tile(copy_of(k0 + 1, 1, true), w, lane);
-  const TileCopy none = tile_copy(a, 0, ch.len, 0, 0, false);
-  for (int i = 0; i <= n; ++i) {
-    if (i > 0) {
-      // this wave's copies of tile i are done once at most D newer ones
-      // (tile i + 1's) are outstanding; after the barrier every wave's are,
-      // the probabilities of tile i - 1 are stored and stage (i - 2) & 3 is
-      // free
-      if (i + 1 < n) wait_vm<D>();
-      else wait_vm<0>();
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      barrier();
-    }
-    // tile i + 2 goes into the stage tile i - 2 used; its copies ride on the
-    // output product when there is one, else on the scores
-    const TileCopy c = copy_of(k0 + i + 2, (i + 2) & 3, i + 2 < n);
-    if (i > 0) tile_pv(S, (i - 1) & 3, (i - 1) & 1, lane, lo, c, w);
-    if (i < n) {
-      f32x4 sacc[2];
-      tile_qk(S, i & 3, lane, lo, i > 0 ? none : c, w, sacc);
-      const u16x8 pf = tile_softmax(a, S, sacc, (k0 + i) * kTile, lane, i == 0);
-      *(MLA_LDS u16x8*)((MLA_LDS uint8_t*)s_p + (i & 1) * P_BUF + lo.p + w * 256) = pf;
-    }
+
+  // Iteration i (1 <= i < n) waits for tile i (this wave's copies are done
+  // once at most kDma newer ones, tile i + 1's, are outstanding; after the
+  // barrier every wave's are, and every wave is done with stage (i - 2) & 3),
+  // copies tile i + 2, runs the output product of tile i - 1 beside the
+  // scores of tile i, and then the softmax of tile i.
+  u16x8 p[2];
+  f32x16 sacc;
+  tile_step<true, false, false>(S, 0, 0, p, lane, lo, TileCopy{}, w, sacc);
+  issue_tile(copy_of(k0 + 2, 2), w, lane);
+  set_reference(a, S, sacc, k0 * kTile, lane);
+  probs<true>(a, S, sacc, k0 * kTile, lane, p);
+  for (int i = 1; i < n; ++i) {
+    wait_vm<kDma>();
+    barrier();
+    const TileCopy c = copy_of(k0 + i + 2, (i + 2) & 3);
+    tile_step<true, true, true>(S, i & 3, (i - 1) & 3, p, lane, lo, c, w, sacc);
+    probs<true>(a, S, sacc, (k0 + i) * kTile, lane, p);
   }
-  // every wave is done with the ring and the probabilities once all have
-  // passed this barrier
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  barrier();
+  tile_step<false, true, false>(S, 0, (n - 1) & 3, p, lane, lo, TileCopy{}, w, sacc);
+  // (the last re-reads must land before the stages are reused or the
+  // workgroup ends)
+  wait_vm<0>();
 }
 
 // The chunk's partial: o~ / l (rounded to bf16, like the output it feeds)
-// and its natural-log log-sum-exp.  The row owners publish 1 / l; each wave
-// then scales its columns of the pair's rows.
-__device__ __forceinline__ void write_partial(const DecodeArgs& a, State& S, int64_t slot,
+// and its natural-log log-sum-exp.  A row's sum is split over its two lanes.
+// The accumulator layout gives each lane 8-byte pieces of one row, so a
+// direct store would write 16 bytes of each of 32 rows per instruction; the
+// rows are staged in the (by then idle) ring instead and leave as whole
+// 1 KiB rows, one per store instruction.
+constexpr int O_PITCH = D_LAT * 2 + 16;   // LDS pitch of a staged output row
+static_assert(NW * 32 * O_PITCH <= NSTAGE * STAGE, "the staged rows fit the ring");
+
+__device__ __forceinline__ void write_partial(const DecodeArgs& a, const State& S, int64_t slot,
                                               int w, int lane) {
-  const int lr = lane & 15, lg = lane >> 4;
-  float* s_inv = (float*)((uint8_t*)s_p + P_BUF);
-  float lsum = S.l;
-  lsum = wave_sum_xor(lsum, 16);
-  lsum = wave_sum_xor(lsum, 32);
-  const float lse = lsum > 0.f ? (S.m + __log2f(lsum)) * kLn2 : -INFINITY;
-  if (lg == 0) {
-    const int row = w * 16 + lr;
-    s_inv[row] = lsum > 0.f ? 1.0f / lsum : 0.f;
-    a.part_lse[slot * kRowsPerWG + row] = lse;
-  }
+  const int lc = lane & 31, hh = lane >> 5;
+  mfma_drain();
+  const float lsum = wave_sum_xor(S.l, 32);
+  const int row = w * 32 + lc;
+  if (hh == 0) a.part_lse[slot * kRowsPerWG + row] =
+      lsum > 0.f ? (S.m + __log2f(lsum)) * kLn2 : -INFINITY;
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  // every wave is done with the ring once all have passed this barrier
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier();
-  const int pr = w >> 1, half = w & 1;
+  MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)s_ring + w * 32 * O_PITCH;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = (pr * 2 + j) * 16 + lr;
-    const float inv = s_inv[row];
-    uint16_t* dst =
-        (uint16_t*)a.part_o + (slot * kRowsPerWG + row) * D_LAT + half * DBH * 16 + lg * 4;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DBH; ++db) {
-      const f32x4 v = S.o[j][db] * inv;
-      *(u32x2*)(dst + db * 16) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    for (int g = 0; g < 4; ++g) {
+      const f32x16& v = S.o[db];
+      *(MLA_LDS u32x2*)(st + lc * O_PITCH + (db * 32 + 8 * g + 4 * hh) * 2) =
+          u32x2{pack_bf16x2(v[4 * g] * inv, v[4 * g + 1] * inv),
+                pack_bf16x2(v[4 * g + 2] * inv, v[4 * g + 3] * inv)};
     }
-  }
+  // (each wave reads back only its own rows)
+  uint8_t* dst = (uint8_t*)a.part_o + (slot * kRowsPerWG + w * 32) * (D_LAT * 2) + lane * 16;
+#pragma unroll
+  for (int r = 0; r < 32; ++r)
+    *(u32x4*)(dst + r * (D_LAT * 2)) = *(const MLA_LDS u32x4*)(st + r * O_PITCH + lane * 16);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = uni(threadIdx.x >> 6);
-  const int lr = lane & 15, lg = lane >> 4;
+  const int lc = lane & 31, hh = lane >> 5;
 
   const int64_t nt = plan_total_tiles(a.seqlens, a.batch, a.row_groups, lane);
   if (nt == 0) return;
@@ -493,63 +464,56 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
   const int n = k1 - k0;
   const int64_t slot = g;
 
-  // query rows of this unit; the (query, head) row of lane (lg, lr) is
-  // R = rg*128 + 16w + lr
+  // query rows of this unit; the (query, head) row of lane (hh, lc) is
+  // R = rg*128 + 32w + lc
   const int rows_total = a.q_len * a.n_heads;
   const uint16_t* qlat = (const uint16_t*)a.q_lat;
   const uint16_t* qpe = (const uint16_t*)a.q_pe;
   State S;
-  const int R = ch.rg * kRowsPerWG + w * 16 + lr;
+  const int R = ch.rg * kRowsPerWG + w * 32 + lc;
   const bool valid = R < rows_total;
   const int jq = valid ? R / a.n_heads : 0;
   const int hq = valid ? R % a.n_heads : 0;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int db = 0; db < DBH; ++db) S.o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < DB; ++db) S.o[db] = f32x16{};
   S.m = -INFINITY;
   S.l = 0.f;
   S.lim = valid ? (a.causal ? ch.len - a.q_len + jq + 1 : ch.len) : 0;
   S.tmax = -INFINITY;
   S.redo = false;
-  // the query is loaded right after the first tile's copies are issued, so
-  // that the first wait covers the two together
+  // the query (KS vector loads per lane, issued right after the first two
+  // tiles' copies); lane (hh, lc) holds dims 16ks + 8hh .. +7 of its row for
+  // every k-step ks
   auto load_query = [&]() {
     const int64_t qrow = ((int64_t)ch.b * a.q_len + jq) * a.n_heads + hq;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       u16x8 v;
       if (kk < KS_LAT)
-        v = *(const u16x8*)(qlat + qrow * D_LAT + kk * 32 + lg * 8);
+        v = *(const u16x8*)(qlat + qrow * D_LAT + kk * 16 + hh * 8);
       else
-        v = *(const u16x8*)(qpe + qrow * D_ROPE + (kk - KS_LAT) * 32 + lg * 8);
-      S.q[kk] = valid ? v : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        v = *(const u16x8*)(qpe + qrow * D_ROPE + (kk - KS_LAT) * 16 + hh * 8);
+      S.q[kk] = v;   // (a row past the end reads row 0; its limit 0 masks every key)
     }
   };
 
-  run_pass(a, S, ch, k0, n, w, lane, load_query);
+  run_pass<KS>(a, S, ch, k0, n, w, lane, load_query);
 
   // rare second pass, with the true row maxima as references, when any row
-  // of the workgroup saw a score jump (a row's columns are spread over two
-  // waves, so all rows start again).  Each wave posts its flag in the
-  // probability buffer, which is free once the pass is over.
-  int* s_flag = (int*)s_p;
+  // of the workgroup saw a score jump; every wave posts its flag
   if (lane == 0) s_flag[w] = S.redo ? 1 : 0;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier();
-  const bool any_redo = __ballot(lane < kWaves && s_flag[lane & (kWaves - 1)] != 0) != 0;
+  const bool any_redo = __ballot(lane < NW && s_flag[lane & (NW - 1)] != 0) != 0;
   if (any_redo) {
-    float mx = S.tmax;
-    mx = wave_max_xor(mx, 16);
-    mx = wave_max_xor(mx, 32);
-    S.m = mx;
+    S.m = wave_max_xor(S.tmax, 32);
     S.l = 0.f;
+    mfma_drain();
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int db = 0; db < DBH; ++db) S.o[j][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // (the pass's first barrier follows every wave's read of the flags)
-    run_pass(a, S, ch, k0, n, w, lane, [] {});
+    for (int db = 0; db < DB; ++db) S.o[db] = f32x16{};
+    // (the pass's first copies go into stages 0 and 1: the barrier above
+    // follows every wave's last read of them)
+    run_pass<0>(a, S, ch, k0, n, w, lane, [] {});
   }
   write_partial(a, S, slot, w, lane);
 }
