@@ -293,10 +293,11 @@ __device__ __forceinline__ void later_probs(const DecodeArgs& a, State& S, const
   // (a row without reference gives -inf + inf = NaN, which fmaxf ignores)
   S.tmax = fmaxf(S.tmax, dmx + m_eff);
   S.redo |= dmx > kRefSlack;
+  // (a probability past 2^64 only occurs in a pass that is redone, which
+  // clears the accumulator and the sum; up to 2^128 it stays finite)
 #pragma unroll
   for (int c = 0; c < 8; ++c)
-    pk[c] = pack_bf16x2(fast_exp2(fminf(d[2 * c], kRefSlack)),
-                        fast_exp2(fminf(d[2 * c + 1], kRefSlack)));
+    pk[c] = pack_bf16x2(fast_exp2(d[2 * c]), fast_exp2(d[2 * c + 1]));
 }
 
 // Adds the rounded probabilities to the lane's sum (v_dot2 with ones, so the
@@ -446,13 +447,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
   const int w = uni(threadIdx.x >> 6);
   const int lc = lane & 31, hh = lane >> 5;
 
-  const int64_t nt = plan_total_tiles(a.seqlens, a.batch, a.row_groups, lane);
-  if (nt == 0) return;
-  const int g = plan_chunk_of_block(
-      blockIdx.x, plan_chunks_before(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, lane));
-  if (g < 0) return;
+  int g;
   Chunk ch;
-  if (!plan_find_chunk(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, g, lane, ch)) return;
+  if (!plan_locate(a.seqlens, a.batch, a.row_groups, a.num_wg, blockIdx.x, lane, g, ch)) return;
   if (ch.c == 0 && threadIdx.x == 0) {
     // where the combine pass finds this unit's partials
     const int64_t u = (int64_t)ch.b * a.row_groups + ch.rg;

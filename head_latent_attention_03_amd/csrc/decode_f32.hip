@@ -19,13 +19,9 @@ constexpr int DR_MAX = 32;
 
 __global__ __launch_bounds__(128) void decode_f32_kernel(DecodeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t nt = plan_total_tiles(a.seqlens, a.batch, a.row_groups, lane);
-  if (nt == 0) return;
-  const int g = plan_chunk_of_block(
-      blockIdx.x, plan_chunks_before(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, lane));
-  if (g < 0) return;
+  int g;
   Chunk ch;
-  if (!plan_find_chunk(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, g, lane, ch)) return;
+  if (!plan_locate(a.seqlens, a.batch, a.row_groups, a.num_wg, blockIdx.x, lane, g, ch)) return;
   if (ch.c == 0 && threadIdx.x == 0) {
     // where the combine pass finds this unit's partials
     const int64_t u = (int64_t)ch.b * a.row_groups + ch.rg;

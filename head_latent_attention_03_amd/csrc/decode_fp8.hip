@@ -289,13 +289,9 @@ __global__ __launch_bounds__(64 * NW, 1) void decode_fp8_kernel(DecodeArgs a) {
   const int w = uni(threadIdx.x >> 6);
   const int lr = lane & 15, lg = lane >> 4;
 
-  const int64_t nt = plan_total_tiles(a.seqlens, a.batch, a.row_groups, lane);
-  if (nt == 0) return;
-  const int g = plan_chunk_of_block(
-      blockIdx.x, plan_chunks_before(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, lane));
-  if (g < 0) return;
+  int g;
   Chunk ch;
-  if (!plan_find_chunk(a.seqlens, a.batch, a.row_groups, nt, a.num_wg, g, lane, ch)) return;
+  if (!plan_locate(a.seqlens, a.batch, a.row_groups, a.num_wg, blockIdx.x, lane, g, ch)) return;
   if (ch.c == 0 && threadIdx.x == 0) {
     const int64_t u = (int64_t)ch.b * a.row_groups + ch.rg;
     a.unit_chunks[2 * u] = g;

@@ -159,6 +159,47 @@ __device__ inline bool plan_find_chunk(const int32_t* seqlens, int batch, int ro
   return false;
 }
 
+// The chunk a decode workgroup runs (the three functions above in one pass):
+// false if there is none.  Up to 64 sequences, one lane each, the lengths are
+// read once and the total, the chunk count and the search all come from
+// registers; beyond that the general functions run.
+__device__ inline bool plan_locate(const int32_t* seqlens, int batch, int row_groups, int G,
+                                   int block, int lane, int& g, Chunk& out) {
+  if (batch > 64) {
+    const int64_t nt = plan_total_tiles(seqlens, batch, row_groups, lane);
+    if (nt == 0) return false;
+    g = plan_chunk_of_block(block, plan_chunks_before(seqlens, batch, row_groups, nt, G, lane));
+    return g >= 0 && plan_find_chunk(seqlens, batch, row_groups, nt, G, g, lane, out);
+  }
+  const int len = lane < batch ? seqlens[lane] : 0;
+  const int tiles = tiles_of(len);
+  int part = tiles;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
+  const int64_t nt = (int64_t)uni(part) * row_groups;
+  if (nt == 0) return false;
+  const int splits = plan_splits(tiles, nt, G);
+  const int cnt = splits * row_groups;
+  int incl = cnt;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int o = __shfl_up(incl, m, 64);
+    if (lane >= m) incl += o;
+  }
+  g = plan_chunk_of_block(block, uni(__shfl(incl, 63, 64)));
+  if (g < 0) return false;
+  const uint64_t hit = __ballot(incl > g);
+  const int f = uni(__builtin_ctzll(hit));
+  out.b = f;
+  out.len = uni(__shfl(len, f, 64));
+  out.tiles = tiles_of(out.len);
+  out.splits = uni(__shfl(splits, f, 64));
+  const int off = g - uni(__shfl(incl - cnt, f, 64));
+  out.rg = off / out.splits;
+  out.c = off % out.splits;
+  return true;
+}
+
 // 2^x with the hardware v_exp_f32 (results below 2^-126 flush to 0, which
 // only drops probabilities that small relative to the row's reference)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -42,6 +42,15 @@ def test_bf16_reduced_ragged(seqlens):
     _run_check(inputs.workload(2, batch=len(seqlens), seqlen=seqlens))
 
 
+def test_bf16_more_sequences_than_a_wave():
+    """70 sequences (the split plan's general path, past one lane per sequence), ragged
+    lengths including an empty one, bf16 and fp8 caches."""
+    lens = [int(x) for x in np.random.default_rng(70).integers(0, 160, size=70)]
+    lens[5] = 0
+    _run_check(inputs.workload(2, batch=70, seqlen=lens))
+    _run_check(inputs.workload(4, batch=70, seqlen=lens))
+
+
 def test_bf16_reduced_sharp_softmax():
     """Same shapes with N(0,1)/sqrt(dim) inputs: scores spread out, the softmax is peaked."""
     _run_check(inputs.workload(2, batch=3, seqlen=[700, 4096, 33], init="fan_in"))
