@@ -140,17 +140,29 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
   }
   // lane holds q~^T[n = cb*NB + n0 + lg*4 + r][m = y*16 + lr]
   if constexpr (!FP8) {
+    // the rows go through LDS (the W slice is no longer needed) so that each
+    // store writes 16 contiguous bytes per lane, whole rows per wave
+    constexpr int OP = NB * 2 + 16;            // LDS pitch of a staged row
+    static_assert(AB_M * OP <= AB_K * PITCH, "the staged rows fit");
+    __syncthreads();
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int m = mb * AB_M + y * 16 + lr;
-      if (m >= m_total) continue;
-      uint16_t* o = (uint16_t*)a.q_lat + ((int64_t)m * a.n_heads + h) * AB_N + cb * NB;
+    for (int y = 0; y < 4; ++y)
 #pragma unroll
       for (int x = 0; x < NBLK; ++x) {
         const int n = (w * NBLK + x) * 16 + lg * 4;
-        *(u32x2*)(o + n) = u32x2{pack_bf16x2(acc[x][y][0], acc[x][y][1]),
-                                 pack_bf16x2(acc[x][y][2], acc[x][y][3])};
+        *(MLA_LDS u32x2*)((MLA_LDS uint8_t*)s_w + (y * 16 + lr) * OP + n * 2) =
+            u32x2{pack_bf16x2(acc[x][y][0], acc[x][y][1]), pack_bf16x2(acc[x][y][2], acc[x][y][3])};
       }
+    __syncthreads();
+    constexpr int RC = NB / 8;                 // 16-byte chunks per row
+#pragma unroll
+    for (int i = 0; i < AB_M * RC / 256; ++i) {
+      const int c = threadIdx.x + 256 * i;
+      const int ml = c / RC, ch = c % RC;
+      const int m = mb * AB_M + ml;
+      if (m < m_total)
+        *(u32x4*)((uint16_t*)a.q_lat + ((int64_t)m * a.n_heads + h) * AB_N + cb * NB + ch * 8) =
+            *(const MLA_LDS u32x4*)((const MLA_LDS uint8_t*)s_w + ml * OP + ch * 16);
     }
   } else {
     static_assert(NB == AB_N, "the e4m3 row scale needs the whole row");
