@@ -28,10 +28,10 @@
 //   * O^T += C^T P^T: A = 32 latent dims x 16 tokens, two ds_read_b64_tr_b16
 //     (the LDS transpose read) per lane, with the tokens in the order the
 //     score accumulator holds them.
-//   * The output product of tile i - 1 and the scores of tile i are issued
-//     alternately (independent accumulators), so the score chain's MFMA
-//     latency is hidden and the softmax of a tile overlaps nothing but its
-//     own tail.
+//   * Iteration i copies tile i + 2, runs the output product of tile i - 1
+//     and the scores of tile i with their MFMAs alternating (independent
+//     accumulators, so the score chain never waits on its own latency), and
+//     then the softmax of tile i.
 //   * The 32-token tile [c ; k^R] (32 x 1152 B) is brought from HBM straight
 //     into LDS with 16-byte global_load_lds (no VGPR staging), through a ring
 //     of 4 stages: iteration i reads stages i - 1 (output) and i (scores),
@@ -41,25 +41,24 @@
 //     numbers sit one per lane in a VGPR and are read with v_readlane.
 //   * Online softmax in fp32 (base 2, scale folded).  Each row keeps a fixed
 //     reference maximum, set by its first scores, instead of rescaling the
-//     accumulator whenever the maximum grows: probabilities are
-//     exp2(s - m_ref) <= 2^64, so nothing overflows and the accumulator is
-//     only ever written by MFMAs.  If a score passes m_ref + 64 the
-//     workgroup runs its chunk once more with the true row maxima.
-//   * LDS rows are XOR-swizzled on 16-byte chunks so that both read patterns
-//     are bank-conflict free on gfx950's LDS (64 banks of 4 bytes; a 16-byte
-//     read serves its 64 lanes in four 16-lane cycles, lanes taken in quads:
-//     the cycle of lane l is (l >> 5, parity of bits 2..4 of l); an 8-byte
-//     transpose read serves lanes 0-31, then 32-63).  Latent chunk c of
-//     token t sits at slot (c & 15) ^ lat_key(t) of its 256-byte group c >> 4,
-//     lat_key(t) = 4(t & 3) + ((t >> 2) & 3):
+//     accumulator whenever the maximum grows, so the accumulator is only
+//     ever written by MFMAs.  If a score passes m_ref + 64 the workgroup runs
+//     its chunk once more with the true row maxima.
+//   * LDS layout, for gfx950's LDS (64 banks of 4 bytes; a 16-byte read
+//     serves its 64 lanes in four 16-lane cycles, lanes taken in quads: the
+//     cycle of lane l is (l >> 5, parity of bits 2..4 of l); an 8-byte
+//     transpose read serves lanes 0-31, then 32-63).  Latent row t is padded,
+//     at t * 1088 + 16 ((t >> 2) & 3), so its 16-byte chunk c falls in slot
+//     (4t + ((t >> 2) & 3) + c) mod 16 of a 256-byte bank span:
 //       - QK: a cycle's 16 lanes read one chunk of 16 tokens 4a + r whose a
 //         share a parity; (r, a & 3) takes each of its 16 values once;
 //       - PV: a transpose half reads 4 consecutive chunks of 4 consecutive
 //         tokens; 4(t & 3) spreads the tokens over the high two slot bits
-//         while the chunks fill the low two.
-//     Rotary chunk c (0..7) of token t sits at c ^ rope_key(t), rope_key(t)
-//     = ((t >> 2) & 3) + 4((t >> 1) & 1); with the row's 128-byte offset
-//     (bit 0 of t) it separates the 16 tokens of a QK cycle.
+//         while the chunks fill the low two;
+//     and every latent read is one per-lane base plus an immediate.  Rotary
+//     chunk c (0..7) of token t sits at c ^ rope_key(t), rope_key(t) =
+//     ((t >> 2) & 3) + 4((t >> 1) & 1); with the row's 128-byte offset (bit 0
+//     of t) it separates the 16 tokens of a QK cycle.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
