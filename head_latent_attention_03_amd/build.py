@@ -28,11 +28,13 @@ HIPCC_FLAGS = [
     "-Wno-unused-command-line-argument",
 ]
 
-# per-source extra flags: the bf16 decode selects the VGPR form for the MFMAs
-# the compiler emits (the score accumulator is read by VALU code), while its
-# output accumulators are pinned to the accumulation registers by hand
+# per-source extra flags: the bf16 and e4m3 decodes select the VGPR form for
+# the MFMAs the compiler emits (the score accumulators are read by VALU code),
+# while their output accumulators are pinned to the accumulation registers by
+# hand
 EXTRA_FLAGS = {
     "decode_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
