@@ -185,6 +185,7 @@ struct State {
   f32x16 o[DB];         // O^T accumulator: lane holds head l & 31, 16 of the
                         // block's 32 latent dims
   float qs;             // the row's query scale times the softmax scale (log2)
+                        // times s_ref
   int len;              // the sequence length
   float m, l;           // reference max (log2 units, scaled) and per-lane sum
   int lim;              // keys visible to the lane's row: t < lim
@@ -217,22 +218,34 @@ __device__ __forceinline__ LaneOff lane_offsets(int lane) {
   return o;
 }
 
-__device__ __forceinline__ i32x8 load_k(const MLA_LDS uint8_t* kq, const LaneOff& lo, int ks) {
-  const MLA_LDS uint8_t* b = kq + (ks >> 2) * 256;
-  const u32x4 x0 = *(const MLA_LDS u32x4*)(b + (lo.qk ^ (uint32_t)(((4 * ks) & 15) << 4)));
-  const u32x4 x1 = *(const MLA_LDS u32x4*)(b + (lo.qk ^ (uint32_t)((((4 * ks) & 15) ^ 1) << 4)));
+// The reads take the lane's absolute LDS address for a stage (stage base +
+// lane offset): stage bases are multiples of 1 KiB, so the XORed bits 4..7
+// commute with the add, which then happens once per stage and tile instead of
+// once per read.
+__device__ __forceinline__ const MLA_LDS uint8_t* lds_at(uint32_t a) {
+  return (const MLA_LDS uint8_t*)(uintptr_t)a;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const MLA_LDS uint8_t* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+__device__ __forceinline__ i32x8 load_k(uint32_t bq, int ks) {
+  const uint32_t c = (uint32_t)(((4 * ks) & 15) << 4);
+  const u32x4 x0 = *(const MLA_LDS u32x4*)(lds_at(bq ^ c) + (ks >> 2) * 256);
+  const u32x4 x1 = *(const MLA_LDS u32x4*)(lds_at(bq ^ (c ^ 16u)) + (ks >> 2) * 256);
   return __builtin_bit_cast(i32x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-__device__ __forceinline__ u16x8 load_r(const MLA_LDS uint8_t* kq, const LaneOff& lo, int k) {
-  return *(const MLA_LDS u16x8*)(kq + (lo.rp ^ (uint32_t)((2 * k) << 4)));
+__device__ __forceinline__ u16x8 load_r(uint32_t br, int k) {
+  return *(const MLA_LDS u16x8*)lds_at(br ^ (uint32_t)((2 * k) << 4));
 }
 
 // output step j: k-step kb = j >> 4 (tokens 16kb ..), block db = j & 15
-__device__ __forceinline__ long load_v(const MLA_LDS uint8_t* kv, const LaneOff& lo, int j) {
+__device__ __forceinline__ long load_v(uint32_t bv, int j) {
   const int kb = j >> 4, db = j & 15;
   const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-      (MLA_LDS i32x2*)(kv + (lo.pv ^ (uint32_t)((2 * (db & 7)) << 4)) + (db >> 3) * 256 +
+      (MLA_LDS i32x2*)(lds_at(bv ^ (uint32_t)((2 * (db & 7)) << 4)) + (db >> 3) * 256 +
                        kb * 16 * LAT_ROW));
   return __builtin_bit_cast(long, v);
 }
@@ -246,23 +259,23 @@ constexpr int AH = 2;   // LDS reads run this many steps ahead of their MFMAs
 template <bool QK, bool PV, bool COPY>
 __device__ __forceinline__ void tile_step(State& S, int st_qk, int st_pv, long p0, long p1,
                                           int lane, LaneOff lo, const TileCopy& cp, int w,
-                                          f32x16& sl, f32x16& sr) {
+                                          float sr0, f32x16& sl, f32x16& sr) {
   constexpr int NSTEP = PV ? PV_STEPS : KS;
   static_assert(2 * (kDma - 1) < KS, "the copies fit in the score steps");
-  const MLA_LDS uint8_t* kq = stage_base(st_qk);
-  const MLA_LDS uint8_t* kv = stage_base(st_pv);
-  asm volatile("" : "+v"(lo.qk), "+v"(lo.rp), "+v"(lo.pv));
+  const uint32_t bq = lds_addr(stage_base(st_qk)) + lo.qk;
+  const uint32_t br = lds_addr(stage_base(st_qk)) + lo.rp;
+  const uint32_t bv = lds_addr(stage_base(st_pv)) + lo.pv;
   i32x8 ka[AH];
   u16x8 ra[AH];
   long va[AH];
   if (QK) {
     sl = f32x16{};
-    sr = f32x16{};
+    sr = f32x16{} + sr0;
   }
 #pragma unroll
   for (int j = 0; j < AH; ++j) {
-    if (QK) ka[j] = load_k(kq, lo, j);
-    if (PV) va[j] = load_v(kv, lo, j);
+    if (QK) ka[j] = load_k(bq, j);
+    if (PV) va[j] = load_v(bv, j);
   }
 #pragma unroll
   for (int j = 0; j < NSTEP; ++j) {
@@ -270,18 +283,18 @@ __device__ __forceinline__ void tile_step(State& S, int st_qk, int st_pv, long p
     if (COPY && j % 2 == 0 && j / 2 < kDma) issue_part(cp, j / 2, w, lane);
     if (QK && j < KS_LAT) {
       const i32x8 cur = ka[j % AH];
-      if (j + AH < KS_LAT) ka[j % AH] = load_k(kq, lo, j + AH);
-      else ra[(j + AH - KS_LAT) % AH] = load_r(kq, lo, j + AH - KS_LAT);
+      if (j + AH < KS_LAT) ka[j % AH] = load_k(bq, j + AH);
+      else ra[(j + AH - KS_LAT) % AH] = load_r(br, j + AH - KS_LAT);
       sl = mfma_lat(cur, S.q8[j], sl);
     } else if (QK && j < KS) {
       const int k = j - KS_LAT;
       const u16x8 cur = ra[k % AH];
-      if (k + AH < KS_ROPE) ra[k % AH] = load_r(kq, lo, k + AH);
+      if (k + AH < KS_ROPE) ra[k % AH] = load_r(br, k + AH);
       sr = mfma_rope(cur, S.qpe[k], sr);
     }
     if (PV) {
       const long cur = va[j % AH];
-      if (j + AH < PV_STEPS) va[j % AH] = load_v(kv, lo, j + AH);
+      if (j + AH < PV_STEPS) va[j % AH] = load_v(bv, j + AH);
       mfma_pv(S.o[j & (DB - 1)], cur, (j >> 4) ? p1 : p0);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -291,15 +304,17 @@ __device__ __forceinline__ void tile_step(State& S, int st_qk, int st_pv, long p
 // The softmax of one tile.  Lane holds head l & 31 and tokens
 // 8(i >> 2) + 4hh + (i & 3).  On the chunk's first tile (first) a row's
 // first scores set its reference m (the row's two lanes exchange their
-// maxima); later tiles use it as it is, so the output is never rescaled.  A
-// score above m + kSlack (where P' would leave e4m3's range) marks the
-// workgroup for a second pass with the true row maxima.  Returns the e4m3
-// probabilities as the two B operands (tokens 16kb .. of k-step kb) and adds
-// them to the lane's sum.
+// maxima); later tiles use it as it is, so the output is never rescaled, and
+// their rotary accumulator starts at shift = 8 - m, so that the scores arrive
+// already in the exponent of P'.  A score above m + kSlack (where P' would
+// leave e4m3's range) marks the workgroup for a second pass with the true row
+// maxima.  Returns the e4m3 probabilities as the two B operands (tokens
+// 16kb .. of k-step kb) and adds them to the lane's sum.
 __device__ __forceinline__ void tile_probs(const DecodeArgs& a, State& S, const f32x16& sl,
                                            const f32x16& sr, const MLA_LDS uint8_t* base,
                                            int tok0, int w, int lane, float inv_sref,
-                                           float sref_256, bool first, long& p0, long& p1) {
+                                           float sref_256, bool first, float shift0, long& p0,
+                                           long& p1) {
   const int hh = lane >> 5;
   // the per-token factors, once per tile and wave: lane l < 32 forms token
   // l's, the lanes read back the 16 they need (LDS is in order per wave)
@@ -314,36 +329,44 @@ __device__ __forceinline__ void tile_probs(const DecodeArgs& a, State& S, const 
       s_tok[w][1][t] = fb;
     }
   }
-  // the scales of the lane's tokens: 4 groups of 4 consecutive tokens
-  f32x4 sc[4], fa[4], fb[4];
+  // the factors of the lane's tokens: 4 groups of 4 consecutive tokens
+  f32x4 fa[4], fb[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
-    sc[g] = *(const MLA_LDS f32x4*)(base + SCALE_OFF + (8 * g + 4 * hh) * 4);
     fa[g] = *(const MLA_LDS f32x4*)&s_tok[w][0][8 * g + 4 * hh];
     fb[g] = *(const MLA_LDS f32x4*)&s_tok[w][1][8 * g + 4 * hh];
   }
-  // scores in log2 units (the rotary query carries the softmax scale, the
-  // row scale qs the softmax scale too)
+  // scores in log2 units: the latent part is sl * s_t * qs = sl * fa * (qs
+  // s_ref), and the rotary query and qs carry the softmax scale
   float sv[16];
   float mx = -INFINITY;
   const bool cut = __ballot(tok0 + kTile > S.lim) != 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    float v = fmaf(sl[i], sc[i >> 2][i & 3] * S.qs, sr[i]);
+    float v = fmaf(sl[i], fa[i >> 2][i & 3] * S.qs, sr[i]);
     if (cut && tok0 + 8 * (i >> 2) + 4 * hh + (i & 3) >= S.lim) v = -INFINITY;
     sv[i] = v;
     mx = fmaxf(mx, v);
   }
-  S.tmax = fmaxf(S.tmax, mx);
-  if (first && __ballot(mx > S.m + kSlack)) {
-    const float rmx = wave_max_xor(mx, 32);
-    const float mass = wave_sum_xor(S.l, 32);
-    if (rmx > S.m + kSlack && mass == 0.f) S.m = rmx;
+  float shift;
+  if (first) {
+    S.tmax = fmaxf(S.tmax, mx);
+    if (__ballot(mx > S.m + kSlack)) {
+      const float rmx = wave_max_xor(mx, 32);
+      const float mass = wave_sum_xor(S.l, 32);
+      if (rmx > S.m + kSlack && mass == 0.f) S.m = rmx;
+    }
+    S.redo |= mx > S.m + kSlack;
+    // (a row without reference has no visible key: P' = 0)
+    shift = kShift - (S.m == -INFINITY ? INFINITY : S.m);
+  } else {
+    // the scores carry shift0 already; (-inf - -inf = NaN for a row without
+    // reference, which fmaxf ignores)
+    S.tmax = fmaxf(S.tmax, mx - shift0);
+    S.redo |= mx > kShift + kSlack;
+    shift = 0.f;
   }
-  S.redo |= mx > S.m + kSlack;
-  // P' = 2^(s - m + 8) * s_t / s_ref in e4m3, and l += P' * s_ref / (256 s_t);
-  // a row without reference has no visible key (P' = 0)
-  const float shift = kShift - (S.m == -INFINITY ? INFINITY : S.m);
+  // P' = 2^(s - m + 8) * s_t / s_ref in e4m3, and l += P' * s_ref / (256 s_t)
   uint32_t pk[4];
   float lsum = 0.f;
 #pragma unroll
@@ -457,6 +480,7 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
     if (!(sref > 0.f)) sref = 1.f;
     inv_sref = 1.0f / sref;
     sref_256 = sref * (1.0f / 256.0f);
+    S.qs *= sref;
   }
   barrier();
 #pragma unroll
@@ -464,19 +488,21 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
 
   long p0, p1;
   f32x16 sl, sr;
-  tile_step<true, false, false>(S, 0, 0, 0, 0, lane, lo, TileCopy{}, w, sl, sr);
-  tile_probs(a, S, sl, sr, stage_base(0), k0 * kTile, w, lane, inv_sref, sref_256, true, p0,
-             p1);
+  tile_step<true, false, false>(S, 0, 0, 0, 0, lane, lo, TileCopy{}, w, 0.f, sl, sr);
+  tile_probs(a, S, sl, sr, stage_base(0), k0 * kTile, w, lane, inv_sref, sref_256, true, 0.f,
+             p0, p1);
+  const float shift = kShift - (S.m == -INFINITY ? INFINITY : S.m);
   for (int i = 1; i < n; ++i) {
     wait_vm<(AHEAD - 1) * kDma>();
     barrier();
     const int st = i % NSTAGE;
     const TileCopy c = copy_of(k0 + i + AHEAD, (i + AHEAD) % NSTAGE);
-    tile_step<true, true, true>(S, st, (i - 1) % NSTAGE, p0, p1, lane, lo, c, w, sl, sr);
+    tile_step<true, true, true>(S, st, (i - 1) % NSTAGE, p0, p1, lane, lo, c, w, shift, sl, sr);
     tile_probs(a, S, sl, sr, stage_base(st), (k0 + i) * kTile, w, lane, inv_sref, sref_256,
-               false, p0, p1);
+               false, shift, p0, p1);
   }
-  tile_step<false, true, false>(S, 0, (n - 1) % NSTAGE, p0, p1, lane, lo, TileCopy{}, w, sl, sr);
+  tile_step<false, true, false>(S, 0, (n - 1) % NSTAGE, p0, p1, lane, lo, TileCopy{}, w, 0.f, sl,
+                                sr);
   // (the last re-reads must land before the stages are reused or the
   // workgroup ends)
   wait_vm<0>();
