@@ -44,11 +44,28 @@ DECODE_KERNEL_NAME = {"bf16": "decode_bf16_kernel", "f32": "decode_f32_kernel",
                       "fp8": "decode_fp8_kernel"}
 
 
+def _code_lines(text):
+    """The source without // comments, trailing blanks and blank lines (a
+    comment edit does not change the kernel; the sources hold no block
+    comments and no // inside a string)."""
+    out = []
+    for line in text.splitlines():
+        i = line.find("//")
+        if i >= 0:
+            line = line[:i]
+        line = line.rstrip()
+        if line:
+            out.append(line)
+    return "\n".join(out)
+
+
 def source_hash(kind):
+    """Hash of the code (comments stripped) of the sources a decode kernel is
+    built from."""
     h = hashlib.sha256()
     for f in DECODE_SOURCES[kind]:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f)) as fh:
+            h.update(_code_lines(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -191,6 +208,55 @@ def append_time(spec, db, stream, steps):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
 
 
+def e4m3_cache_decode(cfg, launches):
+    """The decode alone over an e4m3 latent cache of the same B=64, L=4096 shape:
+    average launch duration (HIP events on the launch stream) and its roofline
+    figures.  The cache is replicated past the last-level cache, as in the main
+    loop, so every launch reads HBM."""
+    import torch
+    from head_latent_attention_03_amd import inputs
+    from head_latent_attention_03_amd.runner import DeviceBatch
+    spec = inputs.workload(cfg)
+    wl = inputs.make_workload(spec)
+    db = DeviceBatch.from_workload(wl, "cuda:0")
+    cache_bytes = db.kv_latent.numel() * db.kv_latent.element_size() \
+        + db.kv_rope.numel() * db.kv_rope.element_size() + db.kv_scale.numel() * 4
+    n_rep = max(2, math.ceil(2 * MALL_BYTES / cache_bytes))
+    reps = [(db.kv_latent, db.kv_scale, db.kv_rope)]
+    for _ in range(n_rep - 1):
+        reps.append((db.kv_latent.clone(), db.kv_scale.clone(), db.kv_rope.clone()))
+    stream = torch.cuda.current_stream()
+    db.absorb()
+    for i in range(10):
+        lat, sc, rope = reps[i % n_rep]
+        db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for i, (a, b) in enumerate(ev):
+        lat, sc, rope = reps[i % n_rep]
+        a.record(stream)
+        db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    dec_b, dec_f = algorithmic(spec, wl.seqlens)["decode"]
+    gbs = dec_b / (ms * 1e-3) / 1e9
+    tfs = dec_f / (ms * 1e-3) / 1e12
+    traffic = read_traffic("fp8", spec.name)
+    del reps, db
+    torch.cuda.empty_cache()
+    return {
+        "kernel": "mla_decode_paged", "workload": spec.name, "bound": "hbm",
+        "launch_ms": round(ms, 5), "timed_launches": launches, "cache_replicas": n_rep,
+        "algorithmic_bytes": int(dec_b), "algorithmic_flops": int(dec_f),
+        "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "achieved_tflops": round(tfs, 2), "mfma_peak_tflops": MFMA_PEAK_TFLOPS["fp8"],
+        "mfma_frac": round(tfs / MFMA_PEAK_TFLOPS["fp8"], 4),
+    }
+
+
 def cpu_baseline(wl, budget_s):
     """The oracle, as it stands, on a bounded sample of rows of the same workload."""
     import oracle
@@ -224,6 +290,9 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--event-every", type=int, default=8,
                     help="bracket the decode launch of every N-th timed step with HIP events")
+    ap.add_argument("--e4m3-launches", type=int, default=40,
+                    help="time this many decode launches over an e4m3 cache of the same "
+                         "shape after the main loop (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -366,6 +435,8 @@ def main():
         "note": "one wave per new token; at this size the launch latency is the bound, "
                 "not HBM (the bytes would take well under 1 us at 8 TB/s)",
     }
+    if args.e4m3_launches > 0 and args.config == 2:
+        out["e4m3_cache"] = e4m3_cache_decode(4, args.e4m3_launches)
     if args.cpu_budget > 0:
         t_cpu, frac, rows_done, threads = cpu_baseline(wl, args.cpu_budget)
         full_s = t_cpu / frac

@@ -33,11 +33,13 @@
 //     in e4m3 straight from the score registers.
 //   * P' = 2^(s - m + 8) * s_t / s_ref: e4m3 with the row maximum at 256 and
 //     the token scale folded in relative to s_ref, the largest token scale of
-//     the chunk; O accumulates in units of s_ref / 256.  m is a running row
-//     maximum; when a tile's maximum passes m + 0.75 (P' would leave e4m3's
-//     range) m moves to it and O and the sum are rescaled.  The sum l adds
-//     the e4m3-rounded P' back at s_ref / (256 s_t), so numerator and
-//     denominator carry the same rounding.
+//     the chunk; O accumulates in units of s_ref / 256.  m is a fixed row
+//     reference set by the row's first visible scores and never moved, so O
+//     is never rescaled.  A later score past m + 0.75 (where P' would leave
+//     e4m3's range) sends the whole workgroup through a second pass with the
+//     row's true maximum as m.  The sum l adds the e4m3-rounded P' back at
+//     s_ref / (256 s_t), so numerator and denominator carry the same
+//     rounding.
 //   * Iteration i copies tile i + 5 and runs the output product of tile
 //     i - 1 beside the scores of tile i (independent accumulators), then the
 //     softmax of tile i.  A ring of 7 stages [c^ ; k^R ; s] (20.1 KiB each)
