@@ -310,7 +310,7 @@ def main():
                       args.copy_calibration_mib, args.pmc_command)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); there is "
               "no multi-GPU path.  Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

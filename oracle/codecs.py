@@ -6,8 +6,9 @@ bf16: the upper 16 bits of an IEEE-754 binary32 value (1 sign, 8 exponent,
 OCP FP8 E4M3 ("e4m3fn"): 1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
 no infinities, S.1111.111 is NaN, largest finite magnitude 1.75 * 2^8 = 448,
 subnormals m * 2^-9.  The pages name FP8 as the precision of most matrix
-products ([LKVC] "FP8/FP32 Mixed Precision"); the latent-cache quantisation
-that uses it is this build's own reading.
+products ([LKVC] "FP8/FP32 Mixed Precision"); the pages do not spell out a
+latent-cache quantisation, and the per-token scaled one used here is a
+reading of that passage.
 
 Pins: tests compare both codecs with torch's bfloat16 / float8_e4m3fn casts on
 CPU over every code and over random values (a library routine as the pin).
@@ -28,8 +29,8 @@ def bf16_bits_to_f64(bits):
 def f64_to_bf16_bits(x):
     """Round float values to bf16 bit patterns, nearest-even.
 
-    The value is first taken to binary32 (exact for every value this build
-    stores, which are all binary32 to begin with), then its low 16 bits are
+    The value is first taken to binary32 (exact for every value stored here,
+    which are all binary32 to begin with), then its low 16 bits are
     rounded away with ties going to the even result.  NaN maps to 0x7FC0.
     """
     f = np.asarray(x, dtype=np.float32)
@@ -69,9 +70,9 @@ def e4m3_bits_to_f64(bits):
 def f64_to_e4m3_bits(x):
     """Encode to OCP e4m3, nearest-even, saturating finite values at +-448.
 
-    NaN maps to 0x7F.  Saturation (rather than producing NaN on overflow) is
-    this build's choice for the quantiser; the inputs it generates never
-    exceed 448 in magnitude after scaling.
+    NaN maps to 0x7F.  Out-of-range values saturate (rather than becoming
+    NaN), a choice the pages leave open; the quantiser's inputs never exceed
+    448 in magnitude after scaling.
     """
     x = np.asarray(x, dtype=np.float64)
     mag = np.minimum(np.abs(x), E4M3_MAX)

@@ -180,6 +180,46 @@ def test_score_jumps_force_second_pass():
     check_against_oracle(wl, got, rows=sample_rows(wl, 10, seed=4))
 
 
+def test_score_jumps_force_second_pass_fp8_cache():
+    """The e4m3-cache kernel's second pass, taken when a score passes its
+    row's reference by more than 0.75 (log2 units), is right.
+
+    As in the bf16 case the absorbed query is exactly 64 * e_0, whose e4m3
+    code is 448 with row scale 64 / 448.  Latent dim 0 of token t holds k_t:
+    code 448 with token scale k_t / 448 where k_t > 0, code 0 (scale as
+    generated) where k_t = 0; the other dims keep their random codes.  Every
+    score is then 64 * k_t up to the rounding of the scales, on both sides.
+    k_t is 0 for t < 1500, in {11, 12, 13} up to t < 3500 and in {28, 29, 30}
+    after, so with 1024-token chunks the chunks holding t = 1500 and t = 3500
+    see scores far above the reference their first tile set.
+    """
+    from oracle.codecs import f64_to_e4m3_bits
+    spec = inputs.workload(4)
+    wl = inputs.make_workload(spec)
+    rng = np.random.default_rng(8)
+    w_uk = np.zeros((spec.n_heads, spec.d_nope, spec.d_c), dtype=np.float32)
+    w_uk[:, 0, 0] = 1.0
+    wl.w_uk = _bf16_bits(w_uk)
+    q = np.zeros((spec.batch, 1, spec.n_heads, spec.d_nope), dtype=np.float32)
+    q[..., 0] = 64.0
+    wl.q_nope = _bf16_bits(q)
+    wl.q_rope = _bf16_bits(np.zeros((spec.batch, 1, spec.n_heads, spec.d_rope), np.float32))
+    c448 = int(f64_to_e4m3_bits(np.array([448.0]))[0])
+    lat = wl.kv_latent.copy()
+    sc = wl.kv_scale.copy()
+    for b, L in enumerate(wl.seqlens):
+        t = np.arange(int(L))
+        k = np.where(t < 1500, 0, np.where(t < 3500, rng.integers(11, 14, t.size),
+                                           rng.integers(28, 31, t.size)))
+        pg, sl = wl.block_table[b, t // spec.page_size], t % spec.page_size
+        lat[pg, sl, 0] = np.where(k > 0, c448, 0).astype(np.uint8)
+        sc[pg, sl] = np.where(k > 0, k / 448.0, sc[pg, sl]).astype(np.float32)
+    wl.kv_latent = lat
+    wl.kv_scale = sc
+    got = run_library(wl)
+    check_against_oracle(wl, got, rows=sample_rows(wl, 10, seed=4))
+
+
 def test_split_count_invariance():
     """One sequence decoded alone and inside a batch of 64 goes through very
     different split plans: alone, its 128 tiles are spread over one chunk per
