@@ -143,8 +143,10 @@ mla_status_t mla_decode_workspace_size(const mla_dims_t* dims, int32_t batch,
  *   max_seqlen  host-side upper bound of seqlens (sizes the launch)
  *   workspace   at least mla_decode_workspace_size() bytes; receives the
  *             per-split partial outputs and log-sum-exps read by mla_combine
- * Unused cache slots and pages may hold anything (NaN included): they are
- * never read.
+ * Unused cache slots and pages may hold anything (NaN included).  Latent and
+ * rotary rows past a sequence's end are never read; the FP8 scales of the
+ * unused slots of a page the sequence uses are read with their tile and never
+ * reach a result (their tokens' weights are set to zero first).
  */
 mla_status_t mla_decode_paged(const mla_dims_t* dims, int32_t batch, int32_t q_len,
                               int32_t causal, const void* q_latent,
