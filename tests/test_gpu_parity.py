@@ -51,6 +51,24 @@ def test_bf16_more_sequences_than_a_wave():
     _run_check(inputs.workload(4, batch=70, seqlen=lens))
 
 
+@pytest.mark.parametrize("n_heads,q_len,seqlens", [(16, 1, [5, 300, 64]),
+                                                   (200, 3, [3, 300, 1000]),
+                                                   (128, 8, [8, 97])])
+def test_bf16_other_head_counts_and_query_lengths(n_heads, q_len, seqlens):
+    """Head counts that leave a partial 128-row group (16 heads: one group with
+    16 valid rows; 200 heads x 3 query tokens: 600 rows in 5 groups, the last
+    with 88) and the longest supported query run (8 tokens), causal, with a
+    sequence exactly as long as its query run (its first query sees one key)."""
+    _run_check(inputs.workload(2, batch=len(seqlens), n_heads=n_heads, q_len=q_len,
+                               seqlen=seqlens))
+
+
+def test_fp8_cache_other_head_count():
+    """e4m3 cache with 40 heads and 4 query tokens (160 rows: a full group and a
+    partial one), causal."""
+    _run_check(inputs.workload(4, batch=3, n_heads=40, q_len=4, seqlen=[4, 129, 700]))
+
+
 def test_bf16_reduced_sharp_softmax():
     """Same shapes with N(0,1)/sqrt(dim) inputs: scores spread out, the softmax is peaked."""
     _run_check(inputs.workload(2, batch=3, seqlen=[700, 4096, 33], init="fan_in"))
