@@ -69,6 +69,23 @@ def test_fp8_cache_other_head_count():
     _run_check(inputs.workload(4, batch=3, n_heads=40, q_len=4, seqlen=[4, 129, 700]))
 
 
+@pytest.mark.parametrize("case", range(12))
+def test_random_small_shapes(case):
+    """Seeded sweep of small shapes through the whole path, every row against
+    the oracle: bf16 or e4m3 cache, 1-6 sequences of 0-700 tokens (empty ones
+    and ones shorter than their query run included), 1-4 query tokens
+    (causal), 8-136 heads."""
+    rng = np.random.default_rng(1000 + case)
+    cfg = 2 if case % 2 == 0 else 4
+    batch = int(rng.integers(1, 7))
+    q_len = int(rng.integers(1, 5))
+    n_heads = int(rng.choice([8, 16, 40, 64, 128, 136]))
+    lens = [int(x) for x in rng.integers(0, 701, size=batch)]
+    if case % 3 == 0:
+        lens[0] = int(rng.integers(0, q_len + 1))
+    _run_check(inputs.workload(cfg, batch=batch, q_len=q_len, n_heads=n_heads, seqlen=lens))
+
+
 def test_bf16_reduced_sharp_softmax():
     """Same shapes with N(0,1)/sqrt(dim) inputs: scores spread out, the softmax is peaked."""
     _run_check(inputs.workload(2, batch=3, seqlen=[700, 4096, 33], init="fan_in"))
