@@ -36,6 +36,23 @@ def test_tiny_fp32_other_latent_widths(d_c):
     _run_check(inputs.workload(1, d_c=d_c, batch=3, q_len=2, seqlen=[256, 70, 2]))
 
 
+@pytest.mark.parametrize("case", range(8))
+def test_random_small_fp32_shapes(case):
+    """Seeded sweep of the fp32 path over the widths it accepts (latent a
+    multiple of 16 up to 128, even rotary width up to 32, d_nope and d_v up
+    to 128), 1-9 heads, 1-4 sequences of 0-300 tokens, 1-4 query tokens,
+    shuffled or identity block tables; max abs error 1e-4 on every row."""
+    rng = np.random.default_rng(2000 + case)
+    batch = int(rng.integers(1, 5))
+    spec = inputs.workload(
+        1, batch=batch, q_len=int(rng.integers(1, 5)), n_heads=int(rng.integers(1, 10)),
+        d_c=16 * int(rng.integers(1, 9)), d_rope=2 * int(rng.integers(1, 17)),
+        d_nope=int(rng.choice([8, 16, 32, 64, 128])), d_v=int(rng.choice([8, 24, 32, 100, 128])),
+        seqlen=[int(x) for x in rng.integers(0, 301, size=batch)],
+        identity_table=bool(case % 2))
+    _run_check(spec)
+
+
 @pytest.mark.parametrize("seqlens", [[1], [65, 300, 31], [64, 128, 2, 5000]])
 def test_bf16_reduced_ragged(seqlens):
     """DeepSeek-V3 shapes, short and ragged lengths (tails inside a page, one token)."""
