@@ -18,29 +18,30 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // bf16 (d_nope = 128, d_lat = 512): one workgroup per (head h, NB latent
-// columns, 64 rows m).  The W_UK[h] slice [128 x NB] bf16 is staged in LDS and
+// columns, M rows m).  The W_UK[h] slice [128 x NB] bf16 is staged in LDS and
 // read as the A operand of D^T = W_UK[h]^T q^C^T with the LDS transpose read;
-// q^C rows are the B operand straight from global memory.  NB = 256 for bf16
-// output (2 column blocks per head: at 128 heads one workgroup per CU);
-// NB = 512 for e4m3 output, whose per-row scale max|q~| / 448 needs the whole
-// row in one workgroup.
+// q^C rows are the B operand straight from global memory.  NB = 256, M = 64
+// for bf16 output (2 column blocks per head: at 128 heads one workgroup per
+// CU); NB = 512, M = 32 for e4m3 output, whose per-row scale max|q~| / 448
+// needs the whole row in one workgroup (two row blocks per head for 64 rows).
 constexpr int AB_M = 64;
 constexpr int AB_K = 128;    // d_nope
 constexpr int AB_N = 512;    // d_lat
 constexpr int AB_ROPE = 64;  // d_rope
 
-template <int NB, bool FP8>
+template <int NB, bool FP8, int M>
 __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
   // row pitch NB*2 + 32 bytes: the four rows of a transpose-read group land
   // on disjoint banks
   constexpr int PITCH = NB * 2 + 32;
   constexpr int NBLK = NB / 16 / 4;            // 16-column blocks per wave
+  constexpr int NY = M / 16;                    // 16-row blocks
   __shared__ __attribute__((aligned(16))) uint8_t s_w[AB_K * PITCH];
-  __shared__ float s_amax[4][AB_M];
+  __shared__ float s_amax[4][M];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int nmb = (a.batch * a.q_len + AB_M - 1) / AB_M;
+  const int nmb = (a.batch * a.q_len + M - 1) / M;
   constexpr int NCB = AB_N / NB;               // column blocks per head
   const int blk = xcd_logical_id(blockIdx.x, gridDim.x);
   const int h = blk / (nmb * NCB);
@@ -62,10 +63,10 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
     stage[i] = *(const u32x4*)&W[(int64_t)row * AB_N + col * 8];
   }
   // B operand: q^C rows (m = lr within 16-row block y), k = kk*32 + lg*8 ..
-  u16x8 qb[4][AB_K / 32];
+  u16x8 qb[NY][AB_K / 32];
 #pragma unroll
-  for (int y = 0; y < 4; ++y) {
-    const int m = mb * AB_M + y * 16 + lr;
+  for (int y = 0; y < NY; ++y) {
+    const int m = mb * M + y * 16 + lr;
     const bool valid = m < m_total;
     const uint16_t* q = (const uint16_t*)a.q_nope + ((int64_t)(valid ? m : 0) * a.n_heads + h) * AB_K;
 #pragma unroll
@@ -74,10 +75,10 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
       qb[y][kk] = valid ? v : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   }
-  // rotary part: the NCB column blocks of a head split its 64 rows; thread t
+  // rotary part: the NCB column blocks of a head split its M rows; thread t
   // rotates pair t % 32 of rows (t + 256 e) / 32 of this block's share
   constexpr int PAIRS = AB_ROPE / 2;
-  constexpr int RROWS = AB_M / NCB;
+  constexpr int RROWS = M / NCB;
   constexpr int RPER = (RROWS * PAIRS + 255) / 256;
   uint32_t rq[RPER];
   int rpos[RPER];
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
 #pragma unroll
   for (int e = 0; e < RPER; ++e) {
     const int idx = threadIdx.x + e * 256;
-    const int m = mb * AB_M + cb * RROWS + idx / PAIRS;
+    const int m = mb * M + cb * RROWS + idx / PAIRS;
     const bool valid = idx < RROWS * PAIRS && m < m_total;
     const int mm = valid ? m : 0;
     const int64_t off = ((int64_t)mm * a.n_heads + h) * AB_ROPE + 2 * (idx % PAIRS);
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
     for (int e = 0; e < RPER; ++e) {
       if (!rvalid[e]) continue;
       const int idx = threadIdx.x + e * 256;
-      const int m = mb * AB_M + cb * RROWS + idx / PAIRS;
+      const int m = mb * M + cb * RROWS + idx / PAIRS;
       const int64_t off = ((int64_t)m * a.n_heads + h) * AB_ROPE + 2 * (idx % PAIRS);
       float y0, y1;
       rope_pair(__uint_as_float(rq[e] << 16), __uint_as_float(rq[e] & 0xffff0000u), rpos[e],
@@ -117,11 +118,11 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
   __syncthreads();
 
   // wave w: columns n in [w*NB/4, (w+1)*NB/4) of the block = NBLK blocks of 16
-  f32x4 acc[NBLK][4];
+  f32x4 acc[NBLK][NY];
 #pragma unroll
   for (int x = 0; x < NBLK; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int y = 0; y < NY; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < AB_K / 32; ++kk) {
 #pragma unroll
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
       const u16x4 hi = lds_read_tr16(p + 4 * PITCH);
       const u16x8 av = u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-      for (int y = 0; y < 4; ++y) acc[x][y] = mfma_bf16_16x16x32(av, qb[y][kk], acc[x][y]);
+      for (int y = 0; y < NY; ++y) acc[x][y] = mfma_bf16_16x16x32(av, qb[y][kk], acc[x][y]);
     }
   }
   // lane holds q~^T[n = cb*NB + n0 + lg*4 + r][m = y*16 + lr]
@@ -143,10 +144,10 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
     // the rows go through LDS (the W slice is no longer needed) so that each
     // store writes 16 contiguous bytes per lane, whole rows per wave
     constexpr int OP = NB * 2 + 16;            // LDS pitch of a staged row
-    static_assert(AB_M * OP <= AB_K * PITCH, "the staged rows fit");
+    static_assert(M * OP <= AB_K * PITCH, "the staged rows fit");
     __syncthreads();
 #pragma unroll
-    for (int y = 0; y < 4; ++y)
+    for (int y = 0; y < NY; ++y)
 #pragma unroll
       for (int x = 0; x < NBLK; ++x) {
         const int n = (w * NBLK + x) * 16 + lg * 4;
@@ -156,10 +157,10 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
     __syncthreads();
     constexpr int RC = NB / 8;                 // 16-byte chunks per row
 #pragma unroll
-    for (int i = 0; i < AB_M * RC / 256; ++i) {
+    for (int i = 0; i < M * RC / 256; ++i) {
       const int c = threadIdx.x + 256 * i;
       const int ml = c / RC, ch = c % RC;
-      const int m = mb * AB_M + ml;
+      const int m = mb * M + ml;
       if (m < m_total)
         *(u32x4*)((uint16_t*)a.q_lat + ((int64_t)m * a.n_heads + h) * AB_N + cb * NB + ch * 8) =
             *(const MLA_LDS u32x4*)((const MLA_LDS uint8_t*)s_w + ml * OP + ch * 16);
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
     static_assert(NB == AB_N, "the e4m3 row scale needs the whole row");
     // row amax over all 512 columns: lanes -> waves -> LDS
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
+    for (int y = 0; y < NY; ++y) {
       float mx = 0.f;
 #pragma unroll
       for (int x = 0; x < NBLK; ++x)
@@ -180,9 +181,9 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
+    for (int y = 0; y < NY; ++y) {
       const int ml = y * 16 + lr;
-      const int m = mb * AB_M + ml;
+      const int m = mb * M + ml;
       const float amax = fmaxf(fmaxf(s_amax[0][ml], s_amax[1][ml]), fmaxf(s_amax[2][ml], s_amax[3][ml]));
       const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
       const float inv = 1.0f / sc;
@@ -238,14 +239,19 @@ __global__ __launch_bounds__(256) void absorb_f32_kernel(AbsorbArgs a) {
 }  // namespace
 
 hipError_t launch_absorb_bf16(const AbsorbArgs& a, bool fp8_out, hipStream_t s) {
-  const int nmb = (a.batch * a.q_len + AB_M - 1) / AB_M;
-  if (nmb * a.n_heads == 0) return hipSuccess;
+  const int m_total = a.batch * a.q_len;
+  if (m_total * a.n_heads == 0) return hipSuccess;
   if (fp8_out) {
-    hipLaunchKernelGGL((absorb_bf16_kernel<AB_N, true>), dim3((unsigned)(nmb * a.n_heads)),
+    // the e4m3 row scale needs the whole 512-column row in one workgroup: 32
+    // rows per workgroup keep the grid at two workgroups per head for 64 rows
+    constexpr int M = 32;
+    const int nmb = (m_total + M - 1) / M;
+    hipLaunchKernelGGL((absorb_bf16_kernel<AB_N, true, M>), dim3((unsigned)(nmb * a.n_heads)),
                        dim3(256), 0, s, a);
   } else {
-    constexpr int NB = 256;
-    hipLaunchKernelGGL((absorb_bf16_kernel<NB, false>),
+    constexpr int NB = 256, M = AB_M;
+    const int nmb = (m_total + M - 1) / M;
+    hipLaunchKernelGGL((absorb_bf16_kernel<NB, false, M>),
                        dim3((unsigned)(nmb * a.n_heads * (AB_N / NB))), dim3(256), 0, s, a);
   }
   return hipGetLastError();
