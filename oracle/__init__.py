@@ -36,9 +36,8 @@ Parity status of each function is stated in its docstring; nothing here is
 from .codecs import (bf16_bits_to_f64, f64_to_bf16_bits, e4m3_bits_to_f64,
                      f64_to_e4m3_bits, E4M3_MAX)
 from .mla import (rope_theta, apply_rope, gather_cache, expand_kv,
-                  absorb_query, mla_decode_expanded, mla_decode_absorbed,
-                  decode_stored, DecodeResult, inputs_from_workload,
-                  quantize_rows_e4m3)
+                  mla_decode_expanded, mla_decode_absorbed,
+                  decode_stored, DecodeResult, inputs_from_workload)
 from .append import (rms_norm, append_positions, quantize_token_e4m3, append_kv,
                      RMS_EPS)
 from .cache_sizes import (mla_cache_elems_per_token, mha_cache_elems_per_token,
@@ -48,8 +47,8 @@ from .cache_sizes import (mla_cache_elems_per_token, mha_cache_elems_per_token,
 __all__ = [
     "bf16_bits_to_f64", "f64_to_bf16_bits", "e4m3_bits_to_f64",
     "f64_to_e4m3_bits", "E4M3_MAX", "rope_theta", "apply_rope", "gather_cache",
-    "expand_kv", "absorb_query", "mla_decode_expanded", "mla_decode_absorbed",
-    "decode_stored", "DecodeResult", "inputs_from_workload", "quantize_rows_e4m3",
+    "expand_kv", "mla_decode_expanded", "mla_decode_absorbed",
+    "decode_stored", "DecodeResult", "inputs_from_workload",
     "rms_norm", "append_positions", "quantize_token_e4m3", "append_kv", "RMS_EPS",
     "mla_cache_elems_per_token",
     "mha_cache_elems_per_token", "gqa_cache_elems_per_token",

@@ -35,7 +35,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from .codecs import bf16_bits_to_f64, e4m3_bits_to_f64, f64_to_e4m3_bits, E4M3_MAX
+from .codecs import bf16_bits_to_f64, e4m3_bits_to_f64
 
 
 def decode_stored(arr, dtype, scale=None):
@@ -108,14 +108,6 @@ def expand_kv(c, w_uk_h, w_uv_h):
     return c @ w_uk_h.T, c @ w_uv_h.T
 
 
-def absorb_query(q_nope, w_uk):
-    """q~[..., h, :] = W_UK[h]^T q^C[..., h, :]  (the query side of absorption).
-
-    q_nope [..., H, d_nope], w_uk [H, d_nope, d_c] -> [..., H, d_c].
-    """
-    return np.einsum("...hn,hnc->...hc", q_nope, w_uk)
-
-
 @dataclass
 class DecodeResult:
     """Per selected row (b, j, h): everything the three library calls produce."""
@@ -148,7 +140,7 @@ def _visible(length, q_len, j, causal):
     return pos, max(int(n_vis), 0)
 
 
-def _decode(inputs, rows, return_probs, absorbed, query_e4m3=False):
+def _decode(inputs, rows, return_probs, absorbed):
     q_nope = inputs["q_nope"]
     q_rope = inputs["q_rope"]
     w_uk = inputs["w_uk"]
@@ -172,6 +164,8 @@ def _decode(inputs, rows, return_probs, absorbed, query_e4m3=False):
                        q_pe=np.zeros((n, d_r)), o_latent=np.zeros((n, d_c)),
                        out=np.zeros((n, d_v)), lse=np.full(n, -np.inf),
                        n_visible=np.zeros(n, dtype=np.int64), probs=[])
+    # the gathered cache of the current sequence and the expansion of the
+    # current (sequence, head) are kept between consecutive rows that share them
     gathered = {}
     expanded = {}
     for i, (b, j, h) in enumerate(rows):
@@ -186,8 +180,6 @@ def _decode(inputs, rows, return_probs, absorbed, query_e4m3=False):
         qc = q_nope[b, j, h]
         qr = apply_rope(q_rope[b, j, h], pos, base)
         q_lat = w_uk[h].T @ qc
-        if query_e4m3:
-            q_lat = quantize_rows_e4m3(q_lat)
         res.q_latent[i] = q_lat
         res.q_pe[i] = qr
         res.n_visible[i] = n_vis
@@ -199,7 +191,7 @@ def _decode(inputs, rows, return_probs, absorbed, query_e4m3=False):
             s = scale * (c[:n_vis] @ q_lat + kr[:n_vis] @ qr)
         else:
             if h not in expanded:
-                expanded[h] = expand_kv(c, w_uk[h], w_uv[h])
+                expanded = {h: expand_kv(c, w_uk[h], w_uv[h])}
             k_c, v = expanded[h]
             s = scale * (k_c[:n_vis] @ qc + kr[:n_vis] @ qr)
         m = np.max(s)
@@ -236,48 +228,31 @@ def mla_decode_expanded(inputs, rows=None, return_probs=False):
     return _decode(inputs, rows, return_probs, absorbed=False)
 
 
-def mla_decode_absorbed(inputs, rows=None, return_probs=False, query_e4m3=False):
+def mla_decode_absorbed(inputs, rows=None, return_probs=False):
     """Absorbed form: s_t = scale * (q~ . c_t + q_pe . k^R_t), o = W_UV[h] (sum_t p_t c_t).
 
-    Checks that absorption is exact ([LRKV] "Empirical Gains"; [SNAP]).  With
-    ``query_e4m3`` the absorbed query is first replaced by its per-row e4m3
-    form (``quantize_rows_e4m3``), the form an fp8-cache decode multiplies
-    with the e4m3 cache ([LKVC] "FP8/FP32 Mixed Precision").
+    Kept only to check that absorption is exact ([LRKV] "Empirical Gains";
+    [SNAP]): the tests pin it against the expanded form on the same inputs.
     """
-    return _decode(inputs, rows, return_probs, absorbed=True, query_e4m3=query_e4m3)
+    return _decode(inputs, rows, return_probs, absorbed=True)
 
 
-def quantize_rows_e4m3(x):
-    """Each row of x as OCP e4m3 codes times one per-row scale, decoded back.
-
-    The scale is max|row| / 448, so the row's largest magnitude maps to the
-    largest finite e4m3 value (1 for an all-zero row); codes are rounded to
-    nearest-even by this package's own encoder.  Pinned against torch's
-    float8_e4m3fn cast and the e4m3 rounding bound in the tests.
-    """
-    x = np.asarray(x, dtype=np.float64)
-    amax = np.max(np.abs(x), axis=-1, keepdims=True)
-    scale = np.where(amax > 0, amax / E4M3_MAX, 1.0)
-    return e4m3_bits_to_f64(f64_to_e4m3_bits(x / scale)) * scale
-
-
-def inputs_from_workload(wl, latent_override=None):
+def inputs_from_workload(wl):
     """Decode a generated workload's stored arrays into this module's fp64 inputs.
 
     ``wl`` is any object with the generator's fields (spec, kv_latent,
     kv_scale, kv_rope, q_nope, q_rope, w_uk, w_uv, block_table, seqlens); the
-    oracle reads only those stored bits, through its own codecs.
+    oracle reads only those stored bits, through its own codecs.  Pinned
+    field by field on a hand-built workload whose every array holds a
+    different known code (tests/test_oracle_cache_and_inputs.py).
     """
     s = wl.spec
-    lat = latent_override
-    if lat is None:
-        lat = decode_stored(wl.kv_latent, s.latent_dtype, wl.kv_scale)
     return {
         "q_nope": decode_stored(wl.q_nope, s.act_dtype),
         "q_rope": decode_stored(wl.q_rope, s.act_dtype),
         "w_uk": decode_stored(wl.w_uk, s.act_dtype),
         "w_uv": decode_stored(wl.w_uv, s.act_dtype),
-        "kv_latent": lat,
+        "kv_latent": decode_stored(wl.kv_latent, s.latent_dtype, wl.kv_scale),
         "kv_rope": decode_stored(wl.kv_rope, s.act_dtype),
         "block_table": np.asarray(wl.block_table),
         "seqlens": np.asarray(wl.seqlens),

@@ -5,8 +5,8 @@ import numpy as np
 import oracle
 
 
-def oracle_inputs(wl, latent_override=None):
-    return oracle.inputs_from_workload(wl, latent_override)
+def oracle_inputs(wl):
+    return oracle.inputs_from_workload(wl)
 
 
 def random_inputs(rng, batch, q_len, n_heads, d_c, d_rope, d_nope, d_v, seqlens,

@@ -86,3 +86,45 @@ def test_seqlen_rules():
     # arithmetic mean 2048 before clipping (the cap removes a sliver of the tail)
     assert abs(L.mean() - 2048) < 40
     assert abs(np.median(L) - 2048 * math.exp(-0.5)) < 30
+
+
+@pytest.mark.parametrize("latent_dtype", ["bf16", "e4m3"])
+def test_inputs_from_workload_maps_every_field(latent_dtype):
+    """inputs_from_workload on a hand-built workload: every stored array holds its
+    own known code and has its own shape, so a swapped field (W_UK for W_UV, the
+    rotary key for the latent), a wrong decoding or a lost scale shows up.
+    Expected values come from the bf16 / e4m3 format definitions, written out:
+    bf16 0x3F80 = 1, 0x4000 = 2, 0x4040 = 3, 0x4080 = 4, 0x40A0 = 5, 0x40C0 = 6;
+    e4m3 0x40 = 2 (exponent 8 - 7, mantissa 0), times the token scale 0.25."""
+    from types import SimpleNamespace
+    B, S, H, d_c, d_r, d_n, d_v, P, page = 2, 3, 5, 16, 4, 6, 7, 3, 8
+    spec = SimpleNamespace(act_dtype="bf16", latent_dtype=latent_dtype, page_size=page,
+                           rope_base=1234.5, causal=False, scale=lambda: 0.375)
+    full = lambda shape, code, dt=np.uint16: np.full(shape, code, dtype=dt)
+    if latent_dtype == "bf16":
+        kv_latent, kv_scale, lat_val = full((P, page, d_c), 0x40A0), None, 5.0
+    else:
+        kv_latent = full((P, page, d_c), 0x40, np.uint8)
+        kv_scale = np.full((P, page), 0.25, dtype=np.float32)
+        lat_val = 0.5
+    table = np.array([[2, 0], [1, 2]], dtype=np.int32)
+    wl = SimpleNamespace(spec=spec, q_nope=full((B, S, H, d_n), 0x3F80),
+                         q_rope=full((B, S, H, d_r), 0x4000),
+                         w_uk=full((H, d_n, d_c), 0x4040), w_uv=full((H, d_v, d_c), 0x4080),
+                         kv_latent=kv_latent, kv_scale=kv_scale,
+                         kv_rope=full((P, page, d_r), 0x40C0), block_table=table,
+                         seqlens=np.array([9, 16], dtype=np.int32))
+    got = oracle.inputs_from_workload(wl)
+    expect = {"q_nope": ((B, S, H, d_n), 1.0), "q_rope": ((B, S, H, d_r), 2.0),
+              "w_uk": ((H, d_n, d_c), 3.0), "w_uv": ((H, d_v, d_c), 4.0),
+              "kv_latent": ((P, page, d_c), lat_val), "kv_rope": ((P, page, d_r), 6.0)}
+    for name, (shape, val) in expect.items():
+        assert got[name].shape == shape, name
+        assert got[name].dtype == np.float64, name
+        assert np.all(got[name] == val), name
+    assert np.array_equal(got["block_table"], table)
+    assert np.array_equal(got["seqlens"], [9, 16])
+    assert got["page_size"] == page and got["softmax_scale"] == 0.375
+    assert got["rope_base"] == 1234.5 and got["causal"] is False
+    assert set(got) == set(expect) | {"block_table", "seqlens", "page_size", "softmax_scale",
+                                      "rope_base", "causal"}

@@ -59,13 +59,15 @@ def test_e4m3_saturates():
 
 
 def test_row_quantiser_matches_torch_cast_and_bounds():
-    """quantize_rows_e4m3: codes equal torch's float8_e4m3fn cast of row / (max|row|/448),
+    """kernel_models.quantize_rows_e4m3 (the fp8 path's query rounding, a kernel
+    model, not part of the oracle): codes equal torch's float8_e4m3fn cast of row / (max|row|/448),
     the row maximum is kept exactly, and every other value is within half an e4m3 step."""
     rng = np.random.default_rng(2)
     x = rng.standard_normal((64, 512)) * np.exp(rng.uniform(-8, 8, (64, 1)))
     x[3] = 0.0
     x[5, 7] = -abs(x[5]).max() * 2          # a negative row maximum
-    got = oracle.quantize_rows_e4m3(x)
+    import kernel_models
+    got = kernel_models.quantize_rows_e4m3(x)
     amax = np.abs(x).max(axis=1, keepdims=True)
     scale = np.where(amax > 0, amax / 448.0, 1.0)
     codes = torch.from_numpy((x / scale).astype(np.float32)).to(torch.float8_e4m3fn)

@@ -229,24 +229,32 @@ def test_row_subset_matches_full_run():
         assert np.array_equal(sub.o_latent[i], full.o_latent[k])
 
 
-def test_absorbed_with_e4m3_query_moves_only_through_the_query():
-    """With query_e4m3 the absorbed decode equals the absorbed decode fed the quantised
-    query by hand (it changes nothing else), and it differs from the exact one."""
-    from oracle_io import random_inputs
+def test_e4m3_query_kernel_model():
+    """The kernel model of tests/kernel_models.py (the per-row e4m3 query of the
+    fp8-cache path) equals the exact oracle when every absorbed query row is
+    already an e4m3 code times its scale (W_UK[h] the identity, q^C drawn from
+    e4m3 codes with the row maximum at 448 * 2^-4), and moves the result when
+    the query is not representable."""
+    import kernel_models
     rng = np.random.default_rng(41)
-    inp = random_inputs(rng, batch=2, q_len=2, n_heads=3, d_c=32, d_rope=8, d_nope=16,
+    d = 16
+    inp = random_inputs(rng, batch=2, q_len=2, n_heads=3, d_c=d, d_rope=8, d_nope=d,
                         d_v=16, seqlens=[70, 9], page_size=16)
-    a = oracle.mla_decode_absorbed(inp, query_e4m3=True)
-    exact = oracle.mla_decode_absorbed(inp)
-    # redo by hand: quantise q~, then the plain absorbed softmax
-    for i, (b, j, h) in enumerate(a.rows):
-        q8 = oracle.quantize_rows_e4m3(inp["w_uk"][h].T @ inp["q_nope"][b, j, h])
-        assert np.allclose(a.q_latent[i], q8, rtol=0, atol=1e-15)
-        c, kr = oracle.gather_cache(inp["kv_latent"], inp["kv_rope"], inp["block_table"],
-                                    int(b), int(inp["seqlens"][b]), inp["page_size"])
-        n = int(a.n_visible[i])
-        s = inp["softmax_scale"] * (c[:n] @ q8 + kr[:n] @ a.q_pe[i])
-        p = np.exp(s - s.max())
-        p /= p.sum()
-        assert np.allclose(a.o_latent[i], p @ c[:n], rtol=1e-12, atol=1e-14)
-    assert not np.allclose(a.o_latent, exact.o_latent, rtol=1e-6, atol=0)
+    codes = rng.integers(0, 0x7F, size=inp["q_nope"].shape)      # finite e4m3 codes
+    q = oracle.e4m3_bits_to_f64(codes.astype(np.uint8)) * 2.0 ** -4
+    q[..., 0] = 448.0 * 2.0 ** -4                                   # each row's maximum
+    inp["q_nope"] = q
+    inp["w_uk"] = np.broadcast_to(np.eye(d), (3, d, d)).copy()
+    rows = oracle.mla_decode_expanded(inp).rows
+    exact = oracle.mla_decode_expanded(inp, rows=rows)
+    q_lat, o_lat, out, lse = kernel_models.decode_with_e4m3_query(inp, rows)
+    assert np.array_equal(q_lat, exact.q_latent)
+    assert np.allclose(o_lat, exact.o_latent, rtol=1e-12, atol=1e-14)
+    assert np.allclose(out, exact.out, rtol=1e-12, atol=1e-14)
+    assert np.allclose(lse[np.isfinite(lse)], exact.lse[np.isfinite(exact.lse)], rtol=1e-12)
+    # a general query is rounded: the model's result moves away from the oracle's
+    inp2 = random_inputs(rng, batch=2, q_len=2, n_heads=3, d_c=32, d_rope=8, d_nope=16,
+                         d_v=16, seqlens=[70, 9], page_size=16)
+    ex2 = oracle.mla_decode_expanded(inp2)
+    _, o2, _, _ = kernel_models.decode_with_e4m3_query(inp2, ex2.rows)
+    assert not np.allclose(o2, ex2.o_latent, rtol=1e-6, atol=0)
