@@ -147,6 +147,35 @@ def summarize_pmc(fetch_dir, write_dir, kind, workload, copy_mib, commands):
     print(open(path).read())
 
 
+def summarize_trace(db_glob, out_name, title, commands):
+    """Write a kernel-duration summary (profiles/<out_name>) from a rocprofv3
+    --kernel-trace run: calls, mean, median, min and max per kernel."""
+    import sqlite3
+    paths = sorted(glob.glob(db_glob, recursive=True))
+    if not paths:
+        raise SystemExit(f"no rocprofv3 database matches {db_glob}")
+    durs = {}
+    for path in paths:
+        con = sqlite3.connect(path)
+        for name, start, end in con.execute("select name, start, end from kernels"):
+            durs.setdefault(name, []).append((end - start) / 1e3)
+        con.close()
+    out = os.path.join(PROFILES, out_name)
+    total = sum(sum(v) for v in durs.values())
+    with open(out, "w") as fh:
+        fh.write(f"# kernel durations (us): {title}\n")
+        for c in commands:
+            fh.write(f"# command: {c}\n")
+        fh.write(f"{'kernel':72s} {'calls':>5s} {'mean':>8s} {'median':>8s} {'min':>8s} "
+                 f"{'max':>8s} {'share':>6s}\n")
+        for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+            v = np.asarray(v)
+            short = name.replace("mla::(anonymous namespace)::", "")
+            fh.write(f"{short[:72]:72s} {len(v):5d} {v.mean():8.2f} {np.median(v):8.2f} "
+                     f"{v.min():8.2f} {v.max():8.2f} {100 * v.sum() / total:5.1f}%\n")
+    print(open(out).read())
+
+
 def _elt(dt):
     return {"f32": 4, "bf16": 2, "e4m3": 1}[dt]
 
@@ -208,53 +237,122 @@ def append_time(spec, db, stream, steps):
     return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
 
 
-def e4m3_cache_decode(cfg, launches):
-    """The decode alone over an e4m3 latent cache of the same B=64, L=4096 shape:
-    average launch duration (HIP events on the launch stream) and its roofline
-    figures.  The cache is replicated past the last-level cache, as in the main
-    loop, so every launch reads HBM."""
+def kind_of(spec):
+    if spec.act_dtype == "f32":
+        return "f32"
+    return "fp8" if spec.latent_dtype == "e4m3" else "bf16"
+
+
+def replicate_cache(db):
+    """Copies of the cache so that consecutive launches read different copies and
+    together exceed twice the 256 MB last-level cache."""
+    cache_bytes = db.kv_latent.numel() * db.kv_latent.element_size() \
+        + db.kv_rope.numel() * db.kv_rope.element_size() \
+        + (db.kv_scale.numel() * 4 if db.kv_scale is not None else 0)
+    n_rep = max(2, math.ceil(2 * MALL_BYTES / cache_bytes))
+    reps = [(db.kv_latent, db.kv_scale, db.kv_rope)]
+    for _ in range(n_rep - 1):
+        reps.append((db.kv_latent.clone(), None if db.kv_scale is None else db.kv_scale.clone(),
+                     db.kv_rope.clone()))
+    return reps
+
+
+def calibration_copy(mib):
+    """One plain device copy of `mib` MiB (the ruler of the HBM traffic counters)."""
+    import torch
+    n = mib * 2 ** 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def time_decode(db, reps, launches, warm=10):
+    """Durations (ms) of `launches` back-to-back decode launches, each bracketed
+    by HIP events on the launch stream, rotating over the cache replicas."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warm):
+        lat, sc, rope = reps[i % len(reps)]
+        db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for i, (a, b) in enumerate(ev):
+        lat, sc, rope = reps[i % len(reps)]
+        a.record(stream)
+        db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def decode_roofline(spec, seqlens, ms, traffic):
+    """The roofline object of one decode launch shape from its durations (ms)."""
+    kind = kind_of(spec)
+    dec_b, dec_f = algorithmic(spec, seqlens)["decode"]
+    ridge = MFMA_PEAK_TFLOPS[kind] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    bound = "hbm" if dec_f / dec_b < ridge else "mfma"
+    mean = float(np.mean(ms))
+    gbs = dec_b / (mean * 1e-3) / 1e9
+    tfs = dec_f / (mean * 1e-3) / 1e12
+    if bound == "hbm":
+        achieved, peak, unit = gbs, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = tfs, MFMA_PEAK_TFLOPS[kind], "TFLOP/s"
+    return {
+        "kernel": "mla_decode_paged", "workload": spec.name, "bound": bound,
+        "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+        "frac": round(achieved / peak, 4),
+        "traffic": traffic,
+        "traffic_over_algorithmic": None if traffic is None else round(traffic / dec_b, 4),
+        "launch_ms": round(mean, 5),
+        "launch_ms_median": round(float(np.median(ms)), 5),
+        "launch_ms_p10": round(float(np.percentile(ms, 10)), 5),
+        "launch_ms_p90": round(float(np.percentile(ms, 90)), 5),
+        "timed_launches": int(len(ms)),
+        "algorithmic_bytes": int(dec_b), "algorithmic_flops": int(dec_f),
+        "achieved_gbs": round(gbs, 2), "achieved_tflops": round(tfs, 2),
+        "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+        "mfma_frac": round(tfs / MFMA_PEAK_TFLOPS[kind], 4),
+    }
+
+
+def decode_object(cfg, launches, copy_mib=0):
+    """The decode alone on workload `cfg`: `launches` timed launches (HIP events,
+    cache replicated past the last-level cache) and their roofline figures."""
     import torch
     from head_latent_attention_03_amd import inputs
     from head_latent_attention_03_amd.runner import DeviceBatch
     spec = inputs.workload(cfg)
     wl = inputs.make_workload(spec)
     db = DeviceBatch.from_workload(wl, "cuda:0")
-    cache_bytes = db.kv_latent.numel() * db.kv_latent.element_size() \
-        + db.kv_rope.numel() * db.kv_rope.element_size() + db.kv_scale.numel() * 4
-    n_rep = max(2, math.ceil(2 * MALL_BYTES / cache_bytes))
-    reps = [(db.kv_latent, db.kv_scale, db.kv_rope)]
-    for _ in range(n_rep - 1):
-        reps.append((db.kv_latent.clone(), db.kv_scale.clone(), db.kv_rope.clone()))
-    stream = torch.cuda.current_stream()
+    reps = replicate_cache(db)
+    if copy_mib > 0:
+        calibration_copy(copy_mib)
     db.absorb()
-    for i in range(10):
-        lat, sc, rope = reps[i % n_rep]
-        db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(launches)]
-    for i, (a, b) in enumerate(ev):
-        lat, sc, rope = reps[i % n_rep]
-        a.record(stream)
-        db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope)
-        b.record(stream)
-    torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    dec_b, dec_f = algorithmic(spec, wl.seqlens)["decode"]
-    gbs = dec_b / (ms * 1e-3) / 1e9
-    tfs = dec_f / (ms * 1e-3) / 1e12
-    traffic = read_traffic("fp8", spec.name)
+    ms = time_decode(db, reps, launches)
+    out = decode_roofline(spec, wl.seqlens, ms, read_traffic(kind_of(spec), spec.name))
+    out["cache_replicas"] = len(reps)
+    out["tokens_in_cache"] = int(wl.tokens)
+    out["batch"], out["q_len"] = spec.batch, spec.q_len
     del reps, db
     torch.cuda.empty_cache()
-    return {
-        "kernel": "mla_decode_paged", "workload": spec.name, "bound": "hbm",
-        "launch_ms": round(ms, 5), "timed_launches": launches, "cache_replicas": n_rep,
-        "algorithmic_bytes": int(dec_b), "algorithmic_flops": int(dec_f),
-        "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(gbs / HBM_PEAK_GBS, 4),
-        "traffic": traffic,
-        "achieved_tflops": round(tfs, 2), "mfma_peak_tflops": MFMA_PEAK_TFLOPS["fp8"],
-        "mfma_frac": round(tfs / MFMA_PEAK_TFLOPS["fp8"], 4),
-    }
+    return out
+
+
+def cpu_info():
+    """CPU model name and the cores this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
 
 
 def cpu_baseline(wl, budget_s):
@@ -282,31 +380,42 @@ def cpu_baseline(wl, budget_s):
     return t_used, frac, rows_done, threads
 
 
+EXTRA_WORKLOADS = {"e4m3_cache": 4, "long_context": 3, "mtp2": 5}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="bracket the decode launch of every N-th timed step with HIP events")
-    ap.add_argument("--e4m3-launches", type=int, default=40,
-                    help="time this many decode launches over an e4m3 cache of the same "
-                         "shape after the main loop (0: skip)")
+    ap.add_argument("--decode-launches", type=int, default=50,
+                    help="decode launches timed one by one for each roofline object")
+    ap.add_argument("--extra", default="e4m3_cache,long_context,mtp2",
+                    help="comma-separated decode-only objects for the other workloads "
+                         f"({', '.join(EXTRA_WORKLOADS)}; empty: none)")
+    ap.add_argument("--decode-only", type=int, default=0, metavar="N",
+                    help="time only the decode of workload N (for profiling runs) and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="run one plain device copy of this size first (counter calibration)")
+                    help="run one plain device copy of this size before the first decode "
+                         "(counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the decode traffic summary from two rocprofv3 --pmc runs and exit")
     ap.add_argument("--pmc-command", action="append", default=[],
                     help="command lines of the counter runs, recorded in the summary")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("DB_GLOB", "OUT_NAME", "TITLE"),
+                    help="write profiles/OUT_NAME from rocprofv3 --kernel-trace databases "
+                         "(the --pmc-command lines are recorded) and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, args.pmc_command)
+        return
     if args.summarize_pmc:
         from head_latent_attention_03_amd import inputs
-        spec = inputs.workload(args.config)
-        kind = "f32" if spec.act_dtype == "f32" else ("fp8" if spec.latent_dtype == "e4m3" else "bf16")
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], kind, spec.name,
+        spec = inputs.workload(args.decode_only or args.config)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], kind_of(spec), spec.name,
                       args.copy_calibration_mib, args.pmc_command)
         return
     if args.gpus != 1:
@@ -319,75 +428,50 @@ def main():
     from head_latent_attention_03_amd.runner import DeviceBatch
 
     torch.cuda.set_device(0)
+    if args.decode_only:
+        obj = decode_object(args.decode_only, args.decode_launches, args.copy_calibration_mib)
+        print(json.dumps(obj), flush=True)
+        return
+
     spec = inputs.workload(args.config)
     wl = inputs.make_workload(spec)
     db = DeviceBatch.from_workload(wl, "cuda:0")
-    cache_bytes = db.kv_latent.numel() * db.kv_latent.element_size() \
-        + db.kv_rope.numel() * db.kv_rope.element_size() \
-        + (db.kv_scale.numel() * 4 if db.kv_scale is not None else 0)
-    n_rep = max(2, math.ceil(2 * MALL_BYTES / cache_bytes))
-    reps = [(db.kv_latent, db.kv_scale, db.kv_rope)]
-    for _ in range(n_rep - 1):
-        reps.append((db.kv_latent.clone(), None if db.kv_scale is None else db.kv_scale.clone(),
-                     db.kv_rope.clone()))
+    reps = replicate_cache(db)
+    n_rep = len(reps)
     torch.cuda.synchronize()
-
     if args.copy_calibration_mib > 0:
-        n = args.copy_calibration_mib * 2 ** 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").random_(0, 255)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copy(args.copy_calibration_mib)
 
-    stream = torch.cuda.current_stream()
-    # the decode launches of every event_every-th timed step are bracketed by
-    # HIP events (a timing event is not free: bracketing every launch adds
-    # several microseconds per step to the whole-step time)
-    ev_steps = [i for i in range(args.steps) if i % args.event_every == args.event_every - 1]
-    if not ev_steps:
-        ev_steps = [args.steps - 1]
-    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for i in ev_steps}
-
-    def step(i, timed):
+    def step(i):
         lat, sc, rope = reps[i % n_rep]
         db.absorb()
-        if timed and i in ev:
-            ev[i][0].record(stream)
         db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope)
-        if timed and i in ev:
-            ev[i][1].record(stream)
         db.combine(with_uv=True)
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, True)
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev.values()]))
+
+    # the dominant kernel, timed launch by launch in its own loop (HIP events on
+    # the launch stream; the events are kept out of the step loop above, whose
+    # time they would add to)
+    dec_ms = time_decode(db, reps, max(20, args.decode_launches))
+    roof = decode_roofline(spec, wl.seqlens, dec_ms, read_traffic(kind_of(spec), spec.name))
 
     # the cache append of the step's new tokens (the step before decode, timed
-    # on its own after the main loop: it is not part of the metric's step)
-    app_us = append_time(spec, db, stream, args.steps)
+    # on its own: it is not part of the metric's step)
+    app_us = append_time(spec, db, torch.cuda.current_stream(), args.steps)
 
     alg = algorithmic(spec, wl.seqlens)
     step_bytes = sum(v[0] for k, v in alg.items() if k in ("absorb", "decode", "combine"))
     step_flops = sum(v[1] for k, v in alg.items() if k in ("absorb", "decode", "combine"))
-    dec_b, dec_f = alg["decode"]
-    kind = "f32" if spec.act_dtype == "f32" else ("fp8" if spec.latent_dtype == "e4m3" else "bf16")
-    ridge = MFMA_PEAK_TFLOPS[kind] * 1e12 / (HBM_PEAK_GBS * 1e9)
-    bound = "hbm" if dec_f / dec_b < ridge else "mfma"
-    if bound == "hbm":
-        achieved, peak, unit = dec_b / (dec_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
-    else:
-        achieved, peak, unit = dec_f / (dec_ms * 1e-3) / 1e12, MFMA_PEAK_TFLOPS[kind], "TFLOP/s"
-
-    traffic = read_traffic(kind, spec.name)
+    kind = kind_of(spec)
     out = {
         "metric": METRIC,
         "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -410,22 +494,7 @@ def main():
         "tokens_per_s": round(spec.batch * spec.q_len / (ms_step * 1e-3), 1),
         "step_bytes": int(step_bytes),
         "step_flops": int(step_flops),
-        "roofline": {
-            "kernel": "mla_decode_paged",
-            "bound": bound,
-            "achieved": round(achieved, 2),
-            "peak": peak,
-            "unit": unit,
-            "frac": round(achieved / peak, 4),
-            "traffic": traffic,
-            "traffic_over_algorithmic": None if traffic is None else round(traffic / dec_b, 4),
-            "launch_ms": round(dec_ms, 5),
-            "timed_launches": len(ev),
-            "algorithmic_bytes": int(dec_b),
-            "algorithmic_flops": int(dec_f),
-            "achieved_gbs": round(dec_b / (dec_ms * 1e-3) / 1e9, 2),
-            "achieved_tflops": round(dec_f / (dec_ms * 1e-3) / 1e12, 2),
-        },
+        "roofline": roof,
     }
     app_b = alg["append"]
     out["append"] = {
@@ -435,11 +504,15 @@ def main():
         "note": "one wave per new token; at this size the launch latency is the bound, "
                 "not HBM (the bytes would take well under 1 us at 8 TB/s)",
     }
-    if args.e4m3_launches > 0 and args.config == 2:
-        out["e4m3_cache"] = e4m3_cache_decode(4, args.e4m3_launches)
+    del reps, db
+    torch.cuda.empty_cache()
+    if args.config == 2:
+        for name in [x for x in args.extra.split(",") if x]:
+            out[name] = decode_object(EXTRA_WORKLOADS[name], args.decode_launches)
     if args.cpu_budget > 0:
         t_cpu, frac, rows_done, threads = cpu_baseline(wl, args.cpu_budget)
         full_s = t_cpu / frac
+        model, cores = cpu_info()
         out["cpu_baseline"] = {
             "value": round(step_bytes / full_s / 1e9, 6),
             "unit": "GB/s",
@@ -448,6 +521,9 @@ def main():
             "sample": f"{rows_done} of {spec.batch * spec.q_len * spec.n_heads} (b, j, h) rows "
                       f"of the same workload in {t_cpu:.1f} s, scaled to the whole step",
             "seconds_per_step": round(full_s, 2),
+            "cpu_model": model,
+            "cores_available": cores,
+            "threads_note": "cores = the BLAS threads the fp64 oracle ran on",
         }
     print(json.dumps(out), flush=True)
 

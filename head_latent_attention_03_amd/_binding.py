@@ -95,6 +95,9 @@ def load_library(path=LIBRARY_PATH):
     lib.mla_append_kv.argtypes = [dp, i32, i32, _P, _P, _P, ctypes.c_float, i32p, i32p, i32,
                                   _P, _P, _P, i32, _P]
     lib.mla_append_kv.restype = ctypes.c_int
+    lib.mla_validate_paged_host.argtypes = [dp, i32, i32, _P, i32, _P, i32,
+                                            ctypes.POINTER(ctypes.c_int32)]
+    lib.mla_validate_paged_host.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -153,6 +156,22 @@ def mla_absorb_q(dims, q_nope, q_rope, seqlens, w_uk, q_latent, q_latent_scale, 
     _check("mla_absorb_q", lib.mla_absorb_q(
         ctypes.byref(d), B, S, _ptr(q_nope), _ptr(q_rope), _ptr(seqlens), _ptr(w_uk),
         _ptr(q_latent), _ptr(q_latent_scale), _ptr(q_pe), _stream(stream)))
+
+
+def mla_validate_paged_host(dims, num_pages, block_table, seqlens, max_seqlen):
+    """Host check of the decode's block-table and length preconditions on numpy
+    int32 arrays; returns (status code, number of failing sequences)."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seqlens, dtype=np.int32)
+    if bt.ndim != 2 or sl.shape != (bt.shape[0],):
+        raise ValueError("block_table must be [batch, max_pages] and seqlens [batch]")
+    d = dims.c()
+    bad = ctypes.c_int32(-1)
+    code = load_library().mla_validate_paged_host(
+        ctypes.byref(d), bt.shape[0], int(num_pages), bt.ctypes.data_as(_P), bt.shape[1],
+        sl.ctypes.data_as(_P), int(max_seqlen), ctypes.byref(bad))
+    return int(code), int(bad.value)
 
 
 def mla_decode_workspace_size(dims, batch, q_len, max_seqlen):

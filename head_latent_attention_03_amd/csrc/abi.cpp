@@ -5,10 +5,12 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
+#include "mla_validate.hpp"
 
 #define MLA_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -83,7 +85,7 @@ struct Layout {
   int row_groups;
   int num_wg;      // target workgroups G of the split plan
   int grid;        // launched workgroups (>= number of chunks)
-  size_t off_o, off_lse, off_units, bytes;
+  size_t off_o, off_lse, off_units, off_flag, bytes;
 };
 
 Layout layout_for(const mla_dims_t* d, int32_t batch, int32_t q_len, int cus) {
@@ -98,11 +100,42 @@ Layout layout_for(const mla_dims_t* d, int32_t batch, int32_t q_len, int cus) {
   L.off_o = 0;
   L.off_lse = align_up(o_bytes, 256);
   L.off_units = align_up(L.off_lse + slots * mla::kRowsPerWG * 4, 256);
-  L.bytes = align_up(L.off_units + (size_t)units * 2 * 4, 256);
+  L.off_flag = align_up(L.off_units + (size_t)units * 2 * 4, 256);   // MLA_VALIDATE result
+  L.bytes = L.off_flag + 256;
   return L;
 }
 
 mla_status_t launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+// MLA_VALIDATE=1 in the environment (read on every call) turns on the device
+// check of the decode's preconditions.
+bool validation_on() {
+  const char* v = std::getenv("MLA_VALIDATE");
+  return v != nullptr && v[0] == '1' && v[1] == '\0';
+}
+
+// Runs the precondition check on the device, waits for it, and returns
+// MLA_ERR_BAD_SHAPE if any sequence breaks one.
+mla_status_t validate_on_device(const mla_dims_t* d, int32_t batch, int32_t num_pages,
+                                const int32_t* block_table, int32_t max_pages,
+                                const int32_t* seqlens, int32_t max_seqlen, int32_t* flag,
+                                hipStream_t s) {
+  mla::ValidateArgs v;
+  v.block_table = block_table;
+  v.seqlens = seqlens;
+  v.bad = flag;
+  v.batch = batch;
+  v.max_pages = max_pages;
+  v.max_seqlen = max_seqlen;
+  v.page_size = d->page_size;
+  v.num_pages = num_pages;
+  if (mla::launch_validate(v, s) != hipSuccess) return MLA_ERR_HIP;
+  int32_t bad = -1;
+  if (hipMemcpyAsync(&bad, flag, sizeof(bad), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MLA_ERR_HIP;
+  return bad == 0 ? MLA_OK : MLA_ERR_BAD_SHAPE;
+}
 
 }  // namespace
 
@@ -118,6 +151,25 @@ MLA_EXPORT const char* mla_status_string(mla_status_t s) {
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
   }
   return "MLA_ERR_UNKNOWN";
+}
+
+MLA_EXPORT mla_status_t mla_validate_paged_host(const mla_dims_t* dims, int32_t batch,
+                                                int32_t num_pages, const int32_t* block_table,
+                                                int32_t max_pages_per_seq,
+                                                const int32_t* seqlens, int32_t max_seqlen,
+                                                int32_t* bad) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (bad == nullptr || seqlens == nullptr || block_table == nullptr) return MLA_ERR_NULL_POINTER;
+  if (batch < 0 || num_pages < 1 || max_pages_per_seq < 1 || max_seqlen < 0)
+    return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)max_pages_per_seq * dims->page_size < (int64_t)max_seqlen) return MLA_ERR_BAD_SHAPE;
+  int32_t n = 0;
+  for (int32_t b = 0; b < batch; ++b)
+    n += mla::sequence_ok(block_table + (int64_t)b * max_pages_per_seq, seqlens[b], max_seqlen,
+                          max_pages_per_seq, dims->page_size, num_pages) ? 0 : 1;
+  *bad = n;
+  return n == 0 ? MLA_OK : MLA_ERR_BAD_SHAPE;
 }
 
 MLA_EXPORT mla_status_t mla_absorb_q(const mla_dims_t* dims, int32_t batch, int32_t q_len,
@@ -218,9 +270,13 @@ MLA_EXPORT mla_status_t mla_decode_paged(const mla_dims_t* dims, int32_t batch, 
   a.num_wg = L.num_wg;
   a.row_groups = L.row_groups;
   a.scale_log2 = dims->softmax_scale * mla::kLog2e;
-  (void)num_pages;
   DecodeArgs la = a;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (validation_on()) {
+    st = validate_on_device(dims, batch, num_pages, block_table, max_pages_per_seq, seqlens,
+                            max_seqlen, reinterpret_cast<int32_t*>(ws + L.off_flag), s);
+    if (st != MLA_OK) return st;
+  }
   // the launch grid is the chunk-count bound; the kernels read num_wg as G
   hipError_t e;
   if (dims->act_dtype == MLA_F32) {

@@ -319,7 +319,9 @@ __device__ __forceinline__ void tile_probs(const DecodeArgs& a, State& S, const 
                                            long& p1) {
   const int hh = lane >> 5;
   // the per-token factors, once per tile and wave: lane l < 32 forms token
-  // l's, the lanes read back the 16 they need (LDS is in order per wave)
+  // l's, the lanes read back the 16 they need (LDS is in order per wave).
+  // (Scales of visible tokens are normal positive numbers, a precondition of
+  // the call; a zero one would make fb infinite.)
   {
     const int t = lane & 31;
     const float st = *(const MLA_LDS float*)(base + SCALE_OFF + 4 * t);
@@ -433,7 +435,10 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
     for (int u = 0; u < 4; ++u) {
       const int t = t0 + 64 * u + lane;
       const int rel = (t >> 6) - W.pg0;
-      const int page = rel < 64 ? __shfl(W.v, rel & 63, 64) : bt_row[min(t, t_end - 1) >> 6];
+      // (every lane takes part in the shuffle: a lane outside the window
+      // reads the table directly)
+      const int wpage = __shfl(W.v, rel & 63, 64);
+      const int page = rel < 64 ? wpage : bt_row[min(t, t_end - 1) >> 6];
       v[u] = t < t_end ? a.kv_scale[(int64_t)page * kPage + (t & (kPage - 1))] : 0.f;
     }
     sref = fmaxf(sref, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));

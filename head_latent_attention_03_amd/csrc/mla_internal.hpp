@@ -76,4 +76,13 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
+struct ValidateArgs {
+  const int32_t* block_table;  // [batch, max_pages]
+  const int32_t* seqlens;      // [batch]
+  int32_t* bad;                // out: sequences that break a precondition
+  int32_t batch, max_pages, max_seqlen, page_size, num_pages;
+};
+
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
+
 }  // namespace mla

@@ -41,11 +41,20 @@
  *     alignment, shapes, dtype combinations, workspace size) run on the host
  *     before anything is enqueued; a call that returns an error has enqueued
  *     nothing.  MLA_ERR_HIP reports a failed launch.
- *   - Device-side preconditions that are NOT checked (the host cannot see
+ *   - Device-side preconditions, not checked by default (the host cannot see
  *     device memory without a sync): 0 <= block_table entries < num_pages for
  *     every page a sequence uses; 0 <= seqlens[b] <= max_seqlen <=
- *     max_pages_per_seq * page_size.  A row whose query has no visible key
+ *     max_pages_per_seq * page_size; for FP8_E4M3 latents, the scale of every
+ *     visible token is a normal positive number (an all-zero latent row
+ *     carries any such scale: mla_append_kv writes 1; a zero scale is not
+ *     accepted).  A row whose query has no visible key
  *     (seqlens[b] - q_len + j < 0) outputs zeros and LSE = -inf.
+ *   - Validation mode: with the environment variable MLA_VALIDATE set to "1"
+ *     (read on every call), mla_decode_paged first checks the lengths and
+ *     block-table preconditions on the device, waits for that check (the one
+ *     host synchronisation in the library) and returns MLA_ERR_BAD_SHAPE,
+ *     having launched no decode, if any sequence breaks one.
+ *     mla_validate_paged_host runs the same check on host copies.
  *
  * Supported shapes and dtypes (anything else returns MLA_ERR_UNSUPPORTED):
  *   - act BF16, latent BF16 or FP8_E4M3: d_latent = 512, d_rope = 64,
@@ -207,6 +216,24 @@ mla_status_t mla_append_kv(const mla_dims_t* dims, int32_t batch, int32_t q_len,
                            const int32_t* block_table, int32_t max_pages_per_seq,
                            void* kv_latent, float* kv_scale, void* kv_rope,
                            int32_t num_pages, void* stream);
+
+/*
+ * Host-side check of the paged decode's device preconditions on HOST copies
+ * of the lengths and the block table (the check MLA_VALIDATE=1 runs on the
+ * device before a decode).  Sequence b passes when 0 <= seqlens[b] <=
+ * max_seqlen, seqlens[b] <= max_pages_per_seq * page_size, and
+ * 0 <= block_table[b, k] < num_pages for every page k < ceil(seqlens[b] /
+ * page_size) (entries past those pages are never read and may hold anything).
+ *   block_table  HOST [batch, max_pages_per_seq] int32
+ *   seqlens      HOST [batch] int32
+ *   bad          HOST out: the number of sequences that fail
+ * Returns MLA_OK when every sequence passes, MLA_ERR_BAD_SHAPE when some
+ * fail (or an argument is out of range), MLA_ERR_NULL_POINTER for a NULL
+ * pointer.  Touches no device.
+ */
+mla_status_t mla_validate_paged_host(const mla_dims_t* dims, int32_t batch, int32_t num_pages,
+                                     const int32_t* block_table, int32_t max_pages_per_seq,
+                                     const int32_t* seqlens, int32_t max_seqlen, int32_t* bad);
 
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(mla_status_t status);

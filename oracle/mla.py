@@ -164,12 +164,15 @@ def _decode(inputs, rows, return_probs, absorbed):
                        q_pe=np.zeros((n, d_r)), o_latent=np.zeros((n, d_c)),
                        out=np.zeros((n, d_v)), lse=np.full(n, -np.inf),
                        n_visible=np.zeros(n, dtype=np.int64), probs=[])
-    # the gathered cache of the current sequence and the expansion of the
-    # current (sequence, head) are kept between consecutive rows that share them
+    # rows are visited in (b, h, j) order, so that the gathered cache of the
+    # current sequence and the expansion of the current (sequence, head) serve
+    # every row that shares them; results land at the rows' own positions
     gathered = {}
     expanded = {}
-    for i, (b, j, h) in enumerate(rows):
-        b, j, h = int(b), int(j), int(h)
+    probs = [None] * n
+    order = np.lexsort((rows[:, 1], rows[:, 2], rows[:, 0])) if n else []
+    for i in order:
+        b, j, h = (int(x) for x in rows[i])
         length = int(seqlens[b])
         if b not in gathered:
             gathered = {b: gather_cache(kv_latent, kv_rope, block_table, b,
@@ -184,8 +187,7 @@ def _decode(inputs, rows, return_probs, absorbed):
         res.q_pe[i] = qr
         res.n_visible[i] = n_vis
         if n_vis == 0:
-            if return_probs:
-                res.probs.append(np.zeros(0))
+            probs[i] = np.zeros(0)
             continue
         if absorbed:
             s = scale * (c[:n_vis] @ q_lat + kr[:n_vis] @ qr)
@@ -204,8 +206,9 @@ def _decode(inputs, rows, return_probs, absorbed):
             res.out[i] = w_uv[h] @ res.o_latent[i]
         else:
             res.out[i] = p @ v[:n_vis]
-        if return_probs:
-            res.probs.append(p)
+        probs[i] = p
+    if return_probs:
+        res.probs = probs
     return res
 
 

@@ -38,12 +38,8 @@ def run_library(wl, device="cuda:0"):
             "lse_latent": lse_latent, "q_latent": q_lat, "q_pe": to_f64(db.q_pe)}
 
 
-def oracle_rows(wl, rows=None, query_e4m3=False):
-    """The oracle's result on the selected rows.  With query_e4m3 the absorbed
-    form with the e4m3 query (the form the fp8-cache path multiplies), which
-    separates the kernel's own error from the query's quantisation."""
-    if query_e4m3:
-        return oracle.mla_decode_absorbed(oracle_inputs(wl), rows=rows, query_e4m3=True)
+def oracle_rows(wl, rows=None):
+    """The oracle's result (the expanded definition) on the selected rows."""
     return oracle.mla_decode_expanded(oracle_inputs(wl), rows=rows)
 
 
@@ -75,9 +71,9 @@ def kind_of(spec):
     return "fp8" if spec.latent_dtype == "e4m3" else "bf16"
 
 
-def check_against_oracle(wl, got, rows=None, lse_abs=None, query_e4m3=False):
+def check_against_oracle(wl, got, rows=None, lse_abs=None):
     """Compare every output of the step on the selected rows."""
-    ref = oracle_rows(wl, rows, query_e4m3)
+    ref = oracle_rows(wl, rows)
     rws = ref.rows
     kind = kind_of(wl.spec)
     errs = {}
@@ -107,3 +103,33 @@ def sample_rows(wl, n, seed=0):
     rows[-1] = [s.batch - 1, s.q_len - 1, s.n_heads - 1]
     order = np.lexsort((rows[:, 2], rows[:, 1], rows[:, 0]))
     return rows[order]
+
+
+def relative_errors(wl, got, rows=None):
+    """max |gpu - ref| / max |ref| of out and out_latent against the oracle
+    (reported, not asserted)."""
+    ref = oracle_rows(wl, rows)
+    rws = ref.rows
+    res = {}
+    for name, r in (("out", ref.out), ("out_latent", ref.o_latent)):
+        g = gather(got, rws, name)
+        res[name] = float(np.max(np.abs(g - r)) / np.max(np.abs(r)))
+    return res
+
+
+def check_e4m3_kernel_model(wl, got, rows=None):
+    """Kernel-only check of the e4m3-cache path: against tests/kernel_models.py,
+    the oracle's absorbed form with the kernel's own per-row e4m3 query, at the
+    fp8 tolerance.  Not a parity check (the reference carries a kernel step)."""
+    import kernel_models
+    inp = oracle_inputs(wl)
+    if rows is None:
+        s = wl.spec
+        b, j, h = np.meshgrid(np.arange(s.batch), np.arange(s.q_len), np.arange(s.n_heads),
+                              indexing="ij")
+        rows = np.stack([b.ravel(), j.ravel(), h.ravel()], axis=1)
+    q_lat, o_lat, out, lse = kernel_models.decode_with_e4m3_query(inp, rows)
+    errs = {}
+    errs["out"] = assert_close("out", gather(got, rows, "out"), out, "fp8")
+    errs["out_latent"] = assert_close("out_latent", gather(got, rows, "out_latent"), o_lat, "fp8")
+    return errs

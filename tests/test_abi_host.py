@@ -118,3 +118,35 @@ def test_decode_and_combine_argument_checks(lib):
     assert absq(qn=NULL) == 1
     assert absq(qs=A16) == 3                                      # scale with a bf16 latent
     assert absq(qn=A8) == 4
+
+
+def test_validate_paged_host_finds_each_broken_precondition(lib):
+    """mla_validate_paged_host (the check MLA_VALIDATE=1 runs on the device before
+    a decode): each sequence below breaks one precondition, or none; table entries
+    past a sequence's used pages are never read and may hold anything."""
+    import numpy as np
+    d = B.MlaDims(n_heads=128, d_latent=512, d_rope=64, d_nope=128, d_v=128, page_size=64,
+                  softmax_scale=192 ** -0.5, rope_base=10000.0)
+    num_pages, max_pages, max_seqlen = 10, 4, 256
+    good_t = np.array([[3, 1, -7, 99], [0, 9, 2, 5], [4, -1, -1, -1]], dtype=np.int32)
+    good_l = np.array([65, 256, 0], dtype=np.int32)       # pages used: 2, 4, 0
+    assert B.mla_validate_paged_host(d, num_pages, good_t, good_l, max_seqlen) == (0, 0)
+    cases = [
+        ([[3, 10, 0, 0]], [65]),       # a used page past the pool
+        ([[3, -1, 0, 0]], [100]),      # a negative used page
+        ([[3, 1, 0, 0]], [257]),       # longer than max_seqlen
+        ([[3, 1, 0, 0]], [-1]),        # a negative length
+    ]
+    for t, l in cases:
+        code, bad = B.mla_validate_paged_host(d, num_pages, np.array(t, np.int32),
+                                              np.array(l, np.int32), max_seqlen)
+        assert (code, bad) == (2, 1), (t, l, code, bad)
+    # several at once: the count is the number of failing sequences
+    t = np.array([[0, 0, 0, 0], [11, 0, 0, 0], [0, 0, 0, 12]], dtype=np.int32)
+    code, bad = B.mla_validate_paged_host(d, num_pages, t, np.array([256, 1, 193], np.int32),
+                                          max_seqlen)
+    assert (code, bad) == (2, 2)
+    # a table too narrow for max_seqlen is an argument error
+    code, _ = B.mla_validate_paged_host(d, num_pages, good_t[:, :3], good_l, max_seqlen)
+    assert code == 2
+

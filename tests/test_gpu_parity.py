@@ -126,16 +126,41 @@ def test_fp8_cache_reduced_ragged(seqlens):
     _run_check(inputs.workload(4, batch=len(seqlens), seqlen=seqlens))
 
 
-@pytest.mark.parametrize("softmax_scale", [2.0, 8.0])
-def test_fp8_cache_peaked_softmax(softmax_scale):
-    """e4m3 latent with a large softmax scale: peaked rows whose maximum grows from
-    tile to tile, so the running reference moves and the accumulator is rescaled.
+def test_fp8_cache_peaked_softmax():
+    """e4m3 latent with N(0,1)/sqrt(dim) inputs: peaked rows whose maximum grows
+    from tile to tile, against the exact oracle at the fp8 tolerance (6e-2)."""
+    _run_check(inputs.workload(4, batch=3, seqlen=[700, 4096, 33], init="fan_in"))
 
-    At this sharpness the e4m3 query alone moves scores by ~2^-4 relative, so the
-    reference is the oracle's absorbed form with the same per-row e4m3 query; the
-    end-to-end checks against the exact query are the other fp8 tests."""
-    _run_check(inputs.workload(4, batch=3, seqlen=[700, 4096, 33], init="fan_in",
-                               softmax_scale=softmax_scale), query_e4m3=True)
+
+def _sharp_fp8(scale):
+    return inputs.workload(4, batch=3, seqlen=[700, 4096, 33], init="fan_in",
+                           softmax_scale=scale)
+
+
+@pytest.mark.xfail(strict=True, raises=AssertionError,
+                   reason="known accuracy limit of the e4m3-cache path: with a softmax scale "
+                          "of 2 or more on N(0,1)/sqrt(dim) inputs, the per-row e4m3 rounding "
+                          "of the absorbed query (3 mantissa bits) moves the scores past the "
+                          "6e-2 fp8 tolerance of the exact oracle (log-sum-exp 0.11 off at "
+                          "scale 2, outputs ~23% off at scale 8)")
+@pytest.mark.parametrize("softmax_scale", [2.0, 8.0])
+def test_fp8_cache_sharp_softmax_query_rounding_limit(softmax_scale):
+    """Against the exact oracle at 6e-2: expected to fail (strict), so a change in
+    the fp8 path's accuracy shows up here."""
+    _run_check(_sharp_fp8(softmax_scale))
+
+
+@pytest.mark.parametrize("softmax_scale", [2.0, 8.0])
+def test_fp8_cache_sharp_softmax_kernel_only(softmax_scale):
+    """The kernel's own error at sharp softmaxes, separated from the query rounding
+    by the kernel model of tests/kernel_models.py (the oracle's absorbed form fed
+    the same per-row e4m3 query).  A kernel-only check, not a parity test; the
+    exact-oracle error is printed."""
+    from gpu_helpers import check_e4m3_kernel_model, relative_errors
+    wl = inputs.make_workload(_sharp_fp8(softmax_scale))
+    got = run_library(wl)
+    print(f"\n[exact-oracle error, reported] {relative_errors(wl, got)}", flush=True)
+    print(f"[kernel-only errs] {check_e4m3_kernel_model(wl, got)}", flush=True)
 
 
 def test_fp8_cache_two_query_tokens():
