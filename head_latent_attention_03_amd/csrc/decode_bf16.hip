@@ -164,6 +164,66 @@ __device__ __forceinline__ void issue_tile(const TileCopy& c, int w, int lane) {
   for (int j = 0; j < kDma; ++j) issue_part(c, j, w, lane);
 }
 
+// The copies of a tile wholly inside the sequence, with no per-copy address
+// arithmetic: the wave's latent row 8w + j of the tile is base + j KiB, read
+// as base (j < 4) or base + 4 KiB (j >= 4) plus an instruction offset of
+// (j & 3) KiB, and it lands at stage + lat_row(8w + j) = stage + lat_row(8w)
+// + 1088 j + 16 (j >> 2) (for w < 4).  The instruction offset moves the LDS
+// destination too (M0 + offset + 16 lane), so M0 is set that much lower.
+struct FastCopy {
+  const uint8_t* lat;    // latent row 8w of the tile
+  const uint8_t* lat4;   // latent row 8w + 4
+  const uint8_t* rope;   // rotary row 0 of the tile
+  uint32_t m0_lat;       // LDS address of row 8w in the stage
+  uint32_t m0_rope;      // LDS address of the wave's rotary rows in the stage
+};
+
+struct FastLane {
+  uint32_t lat;          // lane * 16
+  uint32_t rope;         // rotary offset of the lane's chunk (see issue_part)
+};
+
+__device__ __forceinline__ constexpr uint32_t lat_row_j(int j) { return 1088u * j + 16u * (j >> 2); }
+static_assert(LAT_PITCH == 1088, "lat_row_j assumes the 1088-byte pitch");
+
+__device__ __forceinline__ FastCopy fast_copy(const DecodeArgs& a, int page, int k, int st, int w) {
+  FastCopy c;
+  const int64_t row0 = (int64_t)page * kPage + ((k * kTile) % kPage);
+  c.lat = (const uint8_t*)a.kv_lat + (row0 + 8 * w) * LAT_ROW;
+  c.lat4 = c.lat + 4 * LAT_ROW;
+  c.rope = (const uint8_t*)a.kv_rope + row0 * ROPE_ROW;
+  const uint32_t sb = (uint32_t)(uintptr_t)stage_base(st);
+  c.m0_lat = uni(sb + lat_row(8 * w));
+  c.m0_rope = uni(sb + LAT_STAGE + w * kLatRows * ROPE_ROW);
+  return c;
+}
+
+template <int J>
+__device__ __forceinline__ void issue_fast(const FastCopy& c, const FastLane& fl) {
+  if constexpr (J < kLatRows) {
+    constexpr int off = (J & 3) * LAT_ROW;
+    constexpr uint32_t m0_add = lat_row_j(J) - (uint32_t)off;
+    const uint8_t* base = J < 4 ? c.lat : c.lat4;
+    asm volatile("s_add_u32 m0, %0, %1\n\tglobal_load_lds_dwordx4 %2, %3 offset:%4"
+                 :
+                 : "s"(c.m0_lat), "i"(m0_add), "v"(fl.lat), "s"(base), "i"(off)
+                 : "memory", "m0", "scc");
+  } else {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(c.m0_rope), "v"(fl.rope), "s"(c.rope)
+                 : "memory", "m0");
+  }
+}
+
+template <int J = 0>
+__device__ __forceinline__ void issue_fast_part(const FastCopy& c, const FastLane& fl, int j) {
+  if constexpr (J < kDma) {
+    if (j == J) issue_fast<J>(c, fl);
+    else issue_fast_part<J + 1>(c, fl, j);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -226,21 +286,18 @@ __device__ __forceinline__ u16x8 load_v(const MLA_LDS uint8_t* kv, const LaneOff
 }
 
 // LDS reads run this many MFMA steps ahead of their use
-#ifdef MLA_AHEAD
-constexpr int AH = MLA_AHEAD;
-#else
 constexpr int AH = 2;
-#endif
 
 // One pipeline step group: the scores of tile stage st_qk (if QK) and the
 // output product of tile stage st_pv with probabilities p (if PV), issued
 // alternately, plus the copies of a later tile (cp), one every kDmaEvery
 // steps.  A copy instruction holds its wave for some 50 cycles; issued ahead
 // of a step's MFMAs, part of that hides behind the MFMA still running.
-template <bool QK, bool PV, bool COPY, int PHASE = 0>
+template <bool QK, bool PV, bool COPY, bool FAST = false>
 __device__ __forceinline__ void tile_step(State& S, int st_qk, int st_pv, const u16x8 (&p)[2],
                                           int lane, LaneOff lo, const TileCopy& cp, int w,
-                                          f32x16& sacc) {
+                                          f32x16& sacc, const FastCopy& fc = FastCopy{},
+                                          const FastLane& fl = FastLane{}) {
   constexpr int NSTEP = QK ? KS : PV_STEPS;
   static_assert(kDmaEvery * (kDma - 1) + kDmaEvery - 1 < KS, "a tile's copies fit in the score steps");
   const MLA_LDS uint8_t* kq = stage_base(st_qk);
@@ -256,8 +313,12 @@ __device__ __forceinline__ void tile_step(State& S, int st_qk, int st_pv, const 
 #pragma unroll
   for (int j = 0; j < NSTEP; ++j) {
     // a copy is issued while the previous step's MFMA still runs
-    if (COPY && j % kDmaEvery == PHASE && j / kDmaEvery < kDma)
-      issue_part(cp, j / kDmaEvery, w, lane);
+    if (COPY && j % kDmaEvery == 0 && j / kDmaEvery < kDma) {
+      if (FAST)
+        issue_fast_part(fc, fl, j / kDmaEvery);
+      else
+        issue_part(cp, j / kDmaEvery, w, lane);
+    }
     if (QK) {
       const u16x8 cur = ka[j % AH];
       if (j + AH < KS) ka[j % AH] = load_k(kq, lo, j + AH);
@@ -390,7 +451,33 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
   issue_tile(copy_of(k0 + 2, 2), w, lane);
   set_reference(a, S, sacc, k0 * kTile, lane);
   probs<true>(a, S, sacc, k0 * kTile, lane, p);
-  for (int i = 1; i < n; ++i) {
+  // Iterations 1 .. n_fast - 1 take the fast path: their tile has no key at
+  // or past any row's limit (no mask: the smallest limit of the rows is
+  // L - q_len + 1 with the causal rule, L without), and the tile they copy
+  // lies wholly inside the sequence (no clamped rows, so every copy address
+  // is a tile base plus loop-invariant offsets).
+  const int lim_min = a.causal ? ch.len - a.q_len + 1 : ch.len;
+  const int mask_free = lim_min >= kTile ? lim_min / kTile - k0 : 0;   // i < mask_free
+  const int copy_free = (k_last + 1) * kTile <= ch.len ? n : n - 3;    // i < copy_free
+  const int n_fast = max(1, min(n, min(mask_free, copy_free)));
+  FastLane fl;
+  fl.lat = (uint32_t)lane << 4;
+  {
+    const int t = w * kLatRows + (lane >> 3);
+    fl.rope = (uint32_t)(t * ROPE_ROW + (((lane & 7) ^ rope_key(t)) << 4));
+  }
+  int i = 1;
+  for (; i < n_fast; ++i) {
+    wait_vm<kDma>();
+    barrier();
+    const int kc = min(k0 + i + 2, k_last);
+    const int page = page_lookup(W, bt_row, a.max_pages, kc * kTile / kPage, lane);
+    const FastCopy fc = fast_copy(a, page, kc, (i + 2) & 3, w);
+    tile_step<true, true, true, true>(S, i & 3, (i - 1) & 3, p, lane, lo, TileCopy{}, w, sacc,
+                                      fc, fl);
+    probs<false>(a, S, sacc, (k0 + i) * kTile, lane, p);
+  }
+  for (; i < n; ++i) {
     wait_vm<kDma>();
     barrier();
     const TileCopy c = copy_of(k0 + i + 2, (i + 2) & 3);
