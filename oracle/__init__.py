@@ -19,6 +19,9 @@ pages it follows:
 * [SLI]   "Deepseek-V3 Define 1: Higher Attachment of Head | by Shirley Li"
   (dataforcee.us), the multi-head-attention part, "Key Value Coverage" (the
   KV cache) and the rotary-embedding part ("Cords (rotating rotation").
+* [LKVC] "Operation Flow" and [LRKV] "Empirical Gains" also fix the dense
+  products around the attention (down-projections, query up-projection,
+  weight-level absorption), in ``projections``.
 * "FP8 Mixed-Precision Training" (eeumee.net, the same tag page as [LKVC]),
   section "Three Main Architectures" (RMSNorm of the compressed key/value in
   FP32), for the cache append.
@@ -40,6 +43,8 @@ from .mla import (rope_theta, apply_rope, gather_cache, expand_kv,
                   decode_stored, DecodeResult, inputs_from_workload)
 from .append import (rms_norm, append_positions, quantize_token_e4m3, append_kv,
                      RMS_EPS)
+from .projections import (down_project, up_project_query, absorb_query_weights,
+                          absorb_output_weights, output_project)
 from .cache_sizes import (mla_cache_elems_per_token, mha_cache_elems_per_token,
                           gqa_cache_elems_per_token, mqa_cache_elems_per_token,
                           gqa_equivalent_groups)
@@ -50,7 +55,8 @@ __all__ = [
     "expand_kv", "mla_decode_expanded", "mla_decode_absorbed",
     "decode_stored", "DecodeResult", "inputs_from_workload",
     "rms_norm", "append_positions", "quantize_token_e4m3", "append_kv", "RMS_EPS",
-    "mla_cache_elems_per_token",
+    "down_project", "up_project_query", "absorb_query_weights", "absorb_output_weights",
+    "output_project", "mla_cache_elems_per_token",
     "mha_cache_elems_per_token", "gqa_cache_elems_per_token",
     "mqa_cache_elems_per_token", "gqa_equivalent_groups",
 ]
