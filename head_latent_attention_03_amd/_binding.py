@@ -22,7 +22,7 @@ _TORCH_DT = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16, MLA_FP8_E4M3: tor
 STATUS = {
     0: "MLA_OK", 1: "MLA_ERR_NULL_POINTER", 2: "MLA_ERR_BAD_SHAPE", 3: "MLA_ERR_BAD_DTYPE",
     4: "MLA_ERR_MISALIGNED", 5: "MLA_ERR_WORKSPACE_TOO_SMALL", 6: "MLA_ERR_UNSUPPORTED",
-    7: "MLA_ERR_HIP",
+    7: "MLA_ERR_HIP", 8: "MLA_ERR_SCRATCH_TOO_SMALL",
 }
 
 
@@ -98,6 +98,9 @@ def load_library(path=LIBRARY_PATH):
     lib.mla_validate_paged_host.argtypes = [dp, i32, i32, _P, i32, _P, i32,
                                             ctypes.POINTER(ctypes.c_int32)]
     lib.mla_validate_paged_host.restype = ctypes.c_int
+    lib.mla_decode_noalloc.argtypes = [dp, i32, i32, i32, _P, _P, _P, _P, _P, _P, i32, _P, i32,
+                                       _P, i32, _P, _P, _P, _P]
+    lib.mla_decode_noalloc.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -254,3 +257,37 @@ def mla_append_kv(dims, kv_c, k_rope, norm_weight, norm_eps, seqlens, block_tabl
         ctypes.byref(d), B, S, _ptr(kv_c), _ptr(k_rope), _ptr(norm_weight), float(norm_eps),
         _ptr(seqlens), _ptr(block_table), block_table.shape[1], _ptr(kv_latent),
         _ptr(kv_scale), _ptr(kv_rope), P, _stream(stream)))
+
+
+def mla_decode_noalloc(dims, q_latent, q_latent_scale, q_pe, kv_latent, kv_scale, kv_rope,
+                       block_table, seqlens, max_seqlen, w_uv, out, lse=None, causal=True,
+                       stream=None):
+    """Decode and merge with the library's static scratch (no workspace); see
+    mla_decode_noalloc in mla_decode.h."""
+    B, S, H = q_latent.shape[0], q_latent.shape[1], dims.n_heads
+    dev = q_latent.device
+    act = dims.act_torch
+    P = kv_latent.shape[0]
+    lat_dt = torch.float8_e4m3fn if dims.latent_dtype == "e4m3" else act
+    _expect("q_latent", q_latent, (B, S, H, dims.d_latent), lat_dt, dev)
+    if dims.latent_dtype == "e4m3":
+        _expect("q_latent_scale", q_latent_scale, (B, S, H), torch.float32, dev)
+        _expect("kv_scale", kv_scale, (P, dims.page_size), torch.float32, dev)
+    _expect("q_pe", q_pe, (B, S, H, dims.d_rope), act, dev)
+    _expect("kv_latent", kv_latent, (P, dims.page_size, dims.d_latent), dims.latent_torch, dev)
+    _expect("kv_rope", kv_rope, (P, dims.page_size, dims.d_rope), act, dev)
+    _expect("block_table", block_table, (B, block_table.shape[1]), torch.int32, dev)
+    _expect("seqlens", seqlens, (B,), torch.int32, dev)
+    if w_uv is not None:
+        _expect("w_uv", w_uv, (H, dims.d_v, dims.d_latent), act, dev)
+        _expect("out", out, (B, S, H, dims.d_v), act, dev)
+    else:
+        _expect("out", out, (B, S, H, dims.d_latent), act, dev)
+    if lse is not None:
+        _expect("lse", lse, (B, S, H), torch.float32, dev)
+    d = dims.c()
+    _check("mla_decode_noalloc", load_library().mla_decode_noalloc(
+        ctypes.byref(d), B, S, int(bool(causal)), _ptr(q_latent), _ptr(q_latent_scale),
+        _ptr(q_pe), _ptr(kv_latent), _ptr(kv_scale), _ptr(kv_rope), P, _ptr(block_table),
+        block_table.shape[1], _ptr(seqlens), int(max_seqlen), _ptr(w_uv), _ptr(out), _ptr(lse),
+        _stream(stream)))

@@ -7,6 +7,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
@@ -107,6 +108,32 @@ Layout layout_for(const mla_dims_t* d, int32_t batch, int32_t q_len, int cus) {
 
 mla_status_t launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// Device scratch of mla_decode_noalloc, in place of a caller workspace: the
+// split partials, their log-sum-exps and the unit table of one decode.  Each
+// device holds its own copy for the life of the process.  Its device address
+// comes from hipGetSymbolAddress, once per device; host code never uses the
+// array's own name as an address.
+constexpr size_t kScratchBytes = (size_t)80 << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on the first call there).
+mla_status_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MLA_ERR_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return MLA_OK;
+}
+
 // MLA_VALIDATE=1 in the environment (read on every call) turns on the device
 // check of the decode's preconditions.
 bool validation_on() {
@@ -149,6 +176,9 @@ MLA_EXPORT const char* mla_status_string(mla_status_t s) {
     case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL: workspace below mla_decode_workspace_size()";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: shape not built into this library";
     case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case MLA_ERR_SCRATCH_TOO_SMALL:
+      return "MLA_ERR_SCRATCH_TOO_SMALL: the launch needs more than mla_decode_noalloc's "
+             "static scratch (MLA_NOALLOC_SCRATCH_BYTES); use mla_decode_paged with a workspace";
   }
   return "MLA_ERR_UNKNOWN";
 }
@@ -368,4 +398,35 @@ MLA_EXPORT mla_status_t mla_combine(const mla_dims_t* dims, int32_t batch, int32
   a.row_groups = L.row_groups;
   a.out_dtype = dims->act_dtype;
   return launch_status(mla::launch_combine(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+MLA_EXPORT mla_status_t mla_decode_noalloc(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                           int32_t causal, const void* q_latent,
+                                           const float* q_latent_scale, const void* q_pe,
+                                           const void* kv_latent, const float* kv_scale,
+                                           const void* kv_rope, int32_t num_pages,
+                                           const int32_t* block_table,
+                                           int32_t max_pages_per_seq, const int32_t* seqlens,
+                                           int32_t max_seqlen, const void* w_uv, void* out,
+                                           float* lse, void* stream) {
+  static_assert(kScratchBytes == (size_t)MLA_NOALLOC_SCRATCH_BYTES, "header and library agree");
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if ((st = check_batch(batch, q_len)) != MLA_OK) return st;
+  if (!out) return MLA_ERR_NULL_POINTER;
+  int cus = 0;
+  if ((st = device_cus(&cus)) != MLA_OK) return st;
+  const Layout L = layout_for(dims, batch, q_len, cus);
+  if (L.bytes > kScratchBytes) return MLA_ERR_SCRATCH_TOO_SMALL;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != MLA_OK) return st;
+  // the same two calls a caller makes with a workspace, on the scratch: the
+  // decode writes every partial, log-sum-exp and unit-table entry the merge
+  // reads, so nothing in the scratch needs clearing between calls
+  st = mla_decode_paged(dims, batch, q_len, causal, q_latent, q_latent_scale, q_pe, kv_latent,
+                        kv_scale, kv_rope, num_pages, block_table, max_pages_per_seq, seqlens,
+                        max_seqlen, ws, kScratchBytes, stream);
+  if (st != MLA_OK) return st;
+  return mla_combine(dims, batch, q_len, ws, kScratchBytes, seqlens, max_seqlen, w_uv, out, lse,
+                     stream);
 }

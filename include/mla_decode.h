@@ -81,7 +81,8 @@ typedef enum {
   MLA_ERR_MISALIGNED = 4,
   MLA_ERR_WORKSPACE_TOO_SMALL = 5,
   MLA_ERR_UNSUPPORTED = 6,
-  MLA_ERR_HIP = 7
+  MLA_ERR_HIP = 7,
+  MLA_ERR_SCRATCH_TOO_SMALL = 8
 } mla_status_t;
 
 typedef enum {
@@ -234,6 +235,37 @@ mla_status_t mla_append_kv(const mla_dims_t* dims, int32_t batch, int32_t q_len,
 mla_status_t mla_validate_paged_host(const mla_dims_t* dims, int32_t batch, int32_t num_pages,
                                      const int32_t* block_table, int32_t max_pages_per_seq,
                                      const int32_t* seqlens, int32_t max_seqlen, int32_t* bad);
+
+/*
+ * Allocation-free decode: mla_decode_paged followed by mla_combine, with the
+ * split partials kept in a static device array of the library instead of a
+ * caller workspace.  For callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It calls no hipMalloc, hipFree or other allocating routine;
+ * the caller still passes (and owns) every input and output.
+ *   Arguments: as for mla_decode_paged and mla_combine (same meaning, layout
+ *   and preconditions; out/lse as for mla_combine, w_uv may be NULL for the
+ *   latent output).
+ *   Scratch: MLA_NOALLOC_SCRATCH_BYTES (80 MiB) per device, held by each GPU
+ *   the library runs on until the process ends.  A launch shape needs
+ *   mla_decode_workspace_size() bytes of it (at 256 compute units, up to
+ *   about 600 partial slots of 128 rows: B * ceil(q_len * n_heads / 128) +
+ *   256 <= ~600, e.g. 128 sequences x 2 query tokens x 128 heads); a larger
+ *   one returns MLA_ERR_SCRATCH_TOO_SMALL having enqueued nothing.
+ *   Concurrency: every call on one GPU uses that GPU's single scratch, so
+ *   calls that overlap on one GPU (other streams, other host threads) race
+ *   and must be serialised by the caller.  Nothing in the scratch needs
+ *   clearing between calls: each decode writes everything its merge reads.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (80u * 1024u * 1024u)
+mla_status_t mla_decode_noalloc(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                int32_t causal, const void* q_latent,
+                                const float* q_latent_scale, const void* q_pe,
+                                const void* kv_latent, const float* kv_scale,
+                                const void* kv_rope, int32_t num_pages,
+                                const int32_t* block_table, int32_t max_pages_per_seq,
+                                const int32_t* seqlens, int32_t max_seqlen, const void* w_uv,
+                                void* out, float* lse, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(mla_status_t status);
