@@ -341,6 +341,111 @@ def decode_object(cfg, launches, copy_mib=0):
     return out
 
 
+def prefill_flops(spec, seqlens):
+    """Algorithmic flops of the non-absorbed path: the expansion (2 d_c (d_nope + d_v)
+    per cached token and head) and the causal attention (2 (d_nope + d_R + d_v) per
+    visible key, query row and head)."""
+    L = seqlens.astype(np.int64)
+    H, S = spec.n_heads, spec.q_len
+    expand = 2 * int(L.sum()) * spec.d_c * (spec.d_nope + spec.d_v) * H
+    vis = sum(int(np.sum(np.clip(L - S + j + 1, 0, None))) for j in range(S))
+    attend = 2 * vis * H * (spec.d_nope + spec.d_rope + spec.d_v)
+    absorbed = 2 * vis * H * (2 * spec.d_c + spec.d_rope)
+    return expand, attend, absorbed
+
+
+def prefill_object(launches):
+    """mla_prefill_paged (expand K^C and V per head, then causal attention) on a
+    chunked-prefill batch: launch durations (HIP events) and the MFMA roofline."""
+    import torch
+    from head_latent_attention_03_amd import inputs
+    from head_latent_attention_03_amd import _binding as B
+    from head_latent_attention_03_amd.runner import dims_of, _to_device
+    spec = inputs.prefill_workload()
+    wl = inputs.make_workload(spec)
+    dev = torch.device("cuda:0")
+    dims = dims_of(spec)
+    t = {k: _to_device(getattr(wl, k), dt, dev) for k, dt in
+         (("q_nope", "bf16"), ("q_rope", "bf16"), ("kv_latent", "bf16"), ("kv_rope", "bf16"),
+          ("w_uk", "bf16"), ("w_uv", "bf16"), ("block_table", "i32"), ("seqlens", "i32"))}
+    ws = torch.empty(B.mla_prefill_workspace_size(dims, spec.batch, wl.max_seqlen),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((spec.batch, spec.q_len, spec.n_heads, spec.d_v), dtype=torch.bfloat16,
+                      device=dev)
+    call = lambda: B.mla_prefill_paged(dims, t["q_nope"], t["q_rope"], t["kv_latent"],
+                                       t["kv_rope"], t["block_table"], t["seqlens"],
+                                       wl.max_seqlen, t["w_uk"], t["w_uv"], ws, out)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for a, b in ev:
+        a.record(stream)
+        call()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    expand, attend, absorbed = prefill_flops(spec, wl.seqlens)
+    mean = float(np.mean(ms))
+    tfs = (expand + attend) / (mean * 1e-3) / 1e12
+    del t, ws, out
+    torch.cuda.empty_cache()
+    return {
+        "kernel": "mla_prefill_paged (expand_kv_kernel + attn_kernel)",
+        "workload": spec.name, "batch": spec.batch, "q_len": spec.q_len,
+        "tokens_in_cache": int(wl.tokens), "bound": "mfma",
+        "achieved": round(tfs, 2), "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+        "frac": round(tfs / MFMA_PEAK_TFLOPS["bf16"], 4),
+        "launch_ms": round(mean, 5), "launch_ms_median": round(float(np.median(ms)), 5),
+        "launch_ms_p10": round(float(np.percentile(ms, 10)), 5),
+        "launch_ms_p90": round(float(np.percentile(ms, 90)), 5), "timed_launches": launches,
+        "algorithmic_flops": int(expand + attend), "expand_flops": int(expand),
+        "attend_flops": int(attend), "absorbed_form_flops": int(absorbed),
+        "query_tokens_per_s": round(spec.batch * spec.q_len / (mean * 1e-3), 1),
+    }
+
+
+def projection_object(launches, tokens=4096, d_model=7168, d_cq=1536, d_c=512, d_r=64):
+    """mla_gemm_bf16 as the latent down-projection of a prefill chunk: [c^Q | c^KV |
+    k^R] = [W^DQ; W^DKV; W^KR] h for `tokens` hidden states (bf16, fp32 accumulate),
+    timed with HIP events, against the bf16 MFMA roofline.  The widths stand in for a
+    DeepSeek-V3-sized layer (the pages give the attention shape, not d_model or d_cq)."""
+    import torch
+    from head_latent_attention_03_amd import _binding as B
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device="cpu").manual_seed(1007)
+    n = d_cq + d_c + d_r
+    h = (torch.randn((tokens, d_model), generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    w = (torch.randn((n, d_model), generator=g) / d_model ** 0.5).to(torch.bfloat16).to(dev)
+    out = torch.empty((tokens, n), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        B.mla_gemm_bf16(h, w, out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(launches)]
+    for a, b in ev:
+        a.record(stream)
+        B.mla_gemm_bf16(h, w, out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    flops = 2 * tokens * n * d_model
+    mean = float(np.mean(ms))
+    tfs = flops / (mean * 1e-3) / 1e12
+    del h, w, out
+    torch.cuda.empty_cache()
+    return {
+        "kernel": "mla_gemm_bf16 (gemm_nt_kernel)",
+        "workload": f"latent-down-projection-t{tokens}-dmodel{d_model}-n{n}",
+        "bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_PEAK_TFLOPS["bf16"],
+        "unit": "TFLOP/s", "frac": round(tfs / MFMA_PEAK_TFLOPS["bf16"], 4),
+        "launch_ms": round(mean, 5), "launch_ms_median": round(float(np.median(ms)), 5),
+        "timed_launches": launches, "algorithmic_flops": int(flops),
+        "algorithmic_bytes": int(2 * (tokens * d_model + n * d_model + tokens * n)),
+    }
+
+
 def cpu_info():
     """CPU model name and the cores this process may run on."""
     model = None
@@ -380,7 +485,8 @@ def cpu_baseline(wl, budget_s):
     return t_used, frac, rows_done, threads
 
 
-EXTRA_WORKLOADS = {"e4m3_cache": 4, "long_context": 3, "mtp2": 5}
+EXTRA_WORKLOADS = {"e4m3_cache": 4, "long_context": 3, "mtp2": 5, "prefill": "prefill",
+                   "projection": "projection"}
 
 
 def main():
@@ -391,7 +497,7 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--decode-launches", type=int, default=50,
                     help="decode launches timed one by one for each roofline object")
-    ap.add_argument("--extra", default="e4m3_cache,long_context,mtp2",
+    ap.add_argument("--extra", default="e4m3_cache,long_context,mtp2,prefill,projection",
                     help="comma-separated decode-only objects for the other workloads "
                          f"({', '.join(EXTRA_WORKLOADS)}; empty: none)")
     ap.add_argument("--decode-only", type=int, default=0, metavar="N",
@@ -508,7 +614,12 @@ def main():
     torch.cuda.empty_cache()
     if args.config == 2:
         for name in [x for x in args.extra.split(",") if x]:
-            out[name] = decode_object(EXTRA_WORKLOADS[name], args.decode_launches)
+            if EXTRA_WORKLOADS[name] == "prefill":
+                out[name] = prefill_object(max(5, args.decode_launches // 5))
+            elif EXTRA_WORKLOADS[name] == "projection":
+                out[name] = projection_object(max(10, args.decode_launches // 2))
+            else:
+                out[name] = decode_object(EXTRA_WORKLOADS[name], args.decode_launches)
     if args.cpu_budget > 0:
         t_cpu, frac, rows_done, threads = cpu_baseline(wl, args.cpu_budget)
         full_s = t_cpu / frac

@@ -101,6 +101,23 @@ def load_library(path=LIBRARY_PATH):
     lib.mla_decode_noalloc.argtypes = [dp, i32, i32, i32, _P, _P, _P, _P, _P, _P, i32, _P, i32,
                                        _P, i32, _P, _P, _P, _P]
     lib.mla_decode_noalloc.restype = ctypes.c_int
+    lib.mla_prefill_workspace_size.argtypes = [dp, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_prefill_workspace_size.restype = ctypes.c_int
+    lib.mla_prefill_paged.argtypes = [dp, i32, i32, _P, _P, _P, _P, i32, _P, i32, _P, i32, _P,
+                                      _P, _P, ctypes.c_size_t, _P, _P, _P]
+    lib.mla_prefill_paged.restype = ctypes.c_int
+    i64 = ctypes.c_int64
+    lib.mla_gemm_bf16.argtypes = [i32, i32, i32, i32, _P, i64, i64, _P, i64, i64, _P, i32, i64,
+                                  i64, _P]
+    lib.mla_gemm_bf16.restype = ctypes.c_int
+    lib.mla_absorb_weights_workspace_size.argtypes = [dp, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.mla_absorb_weights_workspace_size.restype = ctypes.c_int
+    lib.mla_absorb_query_weights.argtypes = [dp, i32, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.mla_absorb_query_weights.restype = ctypes.c_int
+    lib.mla_absorb_output_weights.argtypes = [dp, i32, _P, _P, _P, _P, ctypes.c_size_t, _P]
+    lib.mla_absorb_output_weights.restype = ctypes.c_int
+    lib.mla_query_from_latent.argtypes = [dp, i32, i32, i32, _P, _P, _P, _P, _P, _P, _P]
+    lib.mla_query_from_latent.restype = ctypes.c_int
     lib.mla_status_string.argtypes = [ctypes.c_int]
     lib.mla_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -291,3 +308,114 @@ def mla_decode_noalloc(dims, q_latent, q_latent_scale, q_pe, kv_latent, kv_scale
         _ptr(q_pe), _ptr(kv_latent), _ptr(kv_scale), _ptr(kv_rope), P, _ptr(block_table),
         block_table.shape[1], _ptr(seqlens), int(max_seqlen), _ptr(w_uv), _ptr(out), _ptr(lse),
         _stream(stream)))
+
+
+def mla_prefill_workspace_size(dims, batch, max_seqlen):
+    d = dims.c()
+    n = ctypes.c_size_t(0)
+    _check("mla_prefill_workspace_size", load_library().mla_prefill_workspace_size(
+        ctypes.byref(d), int(batch), int(max_seqlen), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mla_prefill_paged(dims, q_nope, q_rope, kv_latent, kv_rope, block_table, seqlens,
+                      max_seqlen, w_uk, w_uv, workspace, out, lse=None, stream=None):
+    """Non-absorbed causal attention of q_len query tokens per sequence; see
+    mla_prefill_paged in mla_decode.h."""
+    B, S, H = q_nope.shape[0], q_nope.shape[1], dims.n_heads
+    dev = q_nope.device
+    act = dims.act_torch
+    P = kv_latent.shape[0]
+    _expect("q_nope", q_nope, (B, S, H, dims.d_nope), act, dev)
+    _expect("q_rope", q_rope, (B, S, H, dims.d_rope), act, dev)
+    _expect("kv_latent", kv_latent, (P, dims.page_size, dims.d_latent), dims.latent_torch, dev)
+    _expect("kv_rope", kv_rope, (P, dims.page_size, dims.d_rope), act, dev)
+    _expect("block_table", block_table, (B, block_table.shape[1]), torch.int32, dev)
+    _expect("seqlens", seqlens, (B,), torch.int32, dev)
+    _expect("w_uk", w_uk, (H, dims.d_nope, dims.d_latent), act, dev)
+    _expect("w_uv", w_uv, (H, dims.d_v, dims.d_latent), act, dev)
+    _expect("out", out, (B, S, H, dims.d_v), act, dev)
+    if lse is not None:
+        _expect("lse", lse, (B, S, H), torch.float32, dev)
+    if workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the same device")
+    d = dims.c()
+    _check("mla_prefill_paged", load_library().mla_prefill_paged(
+        ctypes.byref(d), B, S, _ptr(q_nope), _ptr(q_rope), _ptr(kv_latent), _ptr(kv_rope), P,
+        _ptr(block_table), block_table.shape[1], _ptr(seqlens), int(max_seqlen), _ptr(w_uk),
+        _ptr(w_uv), _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(out),
+        _ptr(lse), _stream(stream)))
+
+
+def mla_gemm_bf16(a, b, c, stream=None):
+    """c[i] = a[i] @ b[i]^T for 2-D or 3-D (batched) bf16 tensors (a [.., m, k],
+    b [.., n, k], c [.., m, n] bf16 or f32; a 2-D operand is shared by every
+    batch entry); see mla_gemm_bf16 in mla_decode.h."""
+    batch = max(t.shape[0] if t.dim() == 3 else 1 for t in (a, b, c))
+    def geo(t):
+        if t.stride(-1) != 1:
+            raise ValueError("the last dimension must be contiguous")
+        if t.dim() == 3:
+            return t.shape[-2], t.shape[-1], t.stride(-2), t.stride(0)
+        return t.shape[0], t.shape[1], t.stride(0), 0
+    m, k, lda, sa = geo(a)
+    n, kb, ldb, sb = geo(b)
+    mc, nc, ldc, sc = geo(c)
+    if kb != k or mc != m or nc != n:
+        raise ValueError(f"shapes do not chain: a {tuple(a.shape)}, b {tuple(b.shape)}, c {tuple(c.shape)}")
+    if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise ValueError("a and b must be bfloat16")
+    cd = {torch.bfloat16: MLA_BF16, torch.float32: MLA_F32}.get(c.dtype)
+    if cd is None:
+        raise ValueError("c must be bfloat16 or float32")
+    _check("mla_gemm_bf16", load_library().mla_gemm_bf16(
+        batch, m, n, k, _ptr(a), lda, sa, _ptr(b), ldb, sb, _ptr(c), cd, ldc, sc,
+        _stream(stream)))
+
+
+def mla_absorb_weights_workspace_size(dims, d_cq):
+    d = dims.c()
+    n = ctypes.c_size_t(0)
+    _check("mla_absorb_weights_workspace_size", load_library().mla_absorb_weights_workspace_size(
+        ctypes.byref(d), int(d_cq), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mla_absorb_query_weights(dims, w_uq, w_uk, w_q_absorbed, workspace, stream=None):
+    H, dn, dq = w_uq.shape
+    dev = w_uq.device
+    _expect("w_uq", w_uq, (dims.n_heads, dims.d_nope, dq), torch.bfloat16, dev)
+    _expect("w_uk", w_uk, (dims.n_heads, dims.d_nope, dims.d_latent), torch.bfloat16, dev)
+    _expect("w_q_absorbed", w_q_absorbed, (dims.n_heads, dims.d_latent, dq), torch.bfloat16, dev)
+    d = dims.c()
+    _check("mla_absorb_query_weights", load_library().mla_absorb_query_weights(
+        ctypes.byref(d), int(dq), _ptr(w_uq), _ptr(w_uk), _ptr(w_q_absorbed), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_absorb_output_weights(dims, w_o, w_uv, w_o_absorbed, workspace, stream=None):
+    dm = w_o.shape[0]
+    dev = w_o.device
+    _expect("w_o", w_o, (dm, dims.n_heads * dims.d_v), torch.bfloat16, dev)
+    _expect("w_uv", w_uv, (dims.n_heads, dims.d_v, dims.d_latent), torch.bfloat16, dev)
+    _expect("w_o_absorbed", w_o_absorbed, (dm, dims.n_heads * dims.d_latent), torch.bfloat16, dev)
+    d = dims.c()
+    _check("mla_absorb_output_weights", load_library().mla_absorb_output_weights(
+        ctypes.byref(d), int(dm), _ptr(w_o), _ptr(w_uv), _ptr(w_o_absorbed), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def mla_query_from_latent(dims, c_q, w_q_absorbed, w_qr, seqlens, q_latent, q_pe, stream=None):
+    B, S, dq = c_q.shape
+    H = dims.n_heads
+    dev = c_q.device
+    _expect("c_q", c_q, (B, S, dq), torch.bfloat16, dev)
+    _expect("w_q_absorbed", w_q_absorbed, (H, dims.d_latent, dq), torch.bfloat16, dev)
+    _expect("w_qr", w_qr, (H * dims.d_rope, dq), torch.bfloat16, dev)
+    _expect("seqlens", seqlens, (B,), torch.int32, dev)
+    _expect("q_latent", q_latent, (B, S, H, dims.d_latent), torch.bfloat16, dev)
+    _expect("q_pe", q_pe, (B, S, H, dims.d_rope), torch.bfloat16, dev)
+    d = dims.c()
+    _check("mla_query_from_latent", load_library().mla_query_from_latent(
+        ctypes.byref(d), B, S, int(dq), _ptr(c_q), _ptr(w_q_absorbed), _ptr(w_qr), _ptr(seqlens),
+        _ptr(q_latent), _ptr(q_pe), _stream(stream)))

@@ -430,3 +430,223 @@ MLA_EXPORT mla_status_t mla_decode_noalloc(const mla_dims_t* dims, int32_t batch
   return mla_combine(dims, batch, q_len, ws, kScratchBytes, seqlens, max_seqlen, w_uv, out, lse,
                      stream);
 }
+
+namespace {
+constexpr int kMaxPrefillQ = 1 << 16;
+
+// K^C and V rows of every sequence, padded to whole pages
+size_t prefill_bytes(const mla_dims_t* d, int32_t batch, int32_t max_seqlen, int32_t* lpad) {
+  const int32_t lp = (max_seqlen + mla::kPage - 1) / mla::kPage * mla::kPage;
+  if (lpad) *lpad = lp;
+  return align_up(2 * (size_t)batch * d->n_heads * lp * 128 * 2, 256);
+}
+
+mla_status_t check_prefill_dims(const mla_dims_t* d) {
+  mla_status_t st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (d->act_dtype != MLA_BF16 || d->latent_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+}  // namespace
+
+MLA_EXPORT mla_status_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t batch,
+                                                   int32_t max_seqlen, size_t* bytes) {
+  mla_status_t st = check_prefill_dims(dims);
+  if (st != MLA_OK) return st;
+  if (bytes == nullptr) return MLA_ERR_NULL_POINTER;
+  if (batch < 0 || max_seqlen < 0) return MLA_ERR_BAD_SHAPE;
+  *bytes = prefill_bytes(dims, batch, max_seqlen, nullptr);
+  return MLA_OK;
+}
+
+MLA_EXPORT mla_status_t mla_prefill_paged(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                          const void* q_nope, const void* q_rope,
+                                          const void* kv_latent, const void* kv_rope,
+                                          int32_t num_pages, const int32_t* block_table,
+                                          int32_t max_pages_per_seq, const int32_t* seqlens,
+                                          int32_t max_seqlen, const void* w_uk, const void* w_uv,
+                                          void* workspace, size_t workspace_bytes, void* out,
+                                          float* lse, void* stream) {
+  mla_status_t st = check_prefill_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || q_len < 1 || q_len > kMaxPrefillQ) return MLA_ERR_BAD_SHAPE;
+  if (!q_nope || !q_rope || !kv_latent || !kv_rope || !block_table || !seqlens || !w_uk ||
+      !w_uv || !workspace || !out)
+    return MLA_ERR_NULL_POINTER;
+  if (num_pages < 1 || max_pages_per_seq < 1 || max_seqlen < 0) return MLA_ERR_BAD_SHAPE;
+  if ((int64_t)max_pages_per_seq * dims->page_size < (int64_t)max_seqlen) return MLA_ERR_BAD_SHAPE;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(kv_latent) || !aligned16(kv_rope) ||
+      !aligned16(block_table) || !aligned16(seqlens) || !aligned16(w_uk) || !aligned16(w_uv) ||
+      !aligned16(workspace) || !aligned16(out) || (lse && !aligned16(lse)))
+    return MLA_ERR_MISALIGNED;
+  int32_t lpad = 0;
+  const size_t need = prefill_bytes(dims, batch, max_seqlen, &lpad);
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (batch == 0 || max_seqlen == 0) return MLA_OK;
+  mla::PrefillArgs a;
+  a.q_nope = q_nope;
+  a.q_rope = q_rope;
+  a.kv_lat = kv_latent;
+  a.kv_rope = kv_rope;
+  a.block_table = block_table;
+  a.seqlens = seqlens;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  a.kexp = ws;
+  a.vexp = ws + (size_t)batch * dims->n_heads * lpad * 128 * 2;
+  a.out = out;
+  a.lse = lse;
+  a.batch = batch;
+  a.q_len = q_len;
+  a.n_heads = dims->n_heads;
+  a.max_pages = max_pages_per_seq;
+  a.lpad = lpad;
+  a.scale_log2 = dims->softmax_scale * mla::kLog2e;
+  a.rope_base = dims->rope_base;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (validation_on()) {
+    // (the flag goes in the output's first word, rewritten by the kernels)
+    st = validate_on_device(dims, batch, num_pages, block_table, max_pages_per_seq, seqlens,
+                            max_seqlen, reinterpret_cast<int32_t*>(workspace), s);
+    if (st != MLA_OK) return st;
+  }
+  return launch_status(mla::launch_prefill(a, s));
+}
+
+namespace {
+bool fits_i32(int64_t v) { return v >= 0 && v <= INT32_MAX; }
+
+mla_status_t gemm(int32_t batch, int32_t m, int32_t n, int32_t k, const void* a, int64_t lda,
+                  int64_t sa, const void* b, int64_t ldb, int64_t sb, void* c, int32_t c_f32,
+                  int64_t ldc, int64_t sc, hipStream_t s) {
+  mla::GemmArgs g;
+  g.a = a; g.b = b; g.c = c;
+  g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+  g.stride_a = sa; g.stride_b = sb; g.stride_c = sc;
+  g.batch = batch; g.m = m; g.n = n; g.k = k; g.c_f32 = c_f32;
+  return launch_status(mla::launch_gemm_nt(g, s));
+}
+
+mla_status_t transpose(int32_t batch, int32_t rows, int32_t cols, const void* src, void* dst,
+                       hipStream_t s) {
+  mla::TransposeArgs t;
+  t.src = src; t.dst = dst; t.batch = batch; t.rows = rows; t.cols = cols;
+  return launch_status(mla::launch_transpose(t, s));
+}
+
+mla_status_t check_bf16_dims(const mla_dims_t* d) {
+  mla_status_t st = check_dims(d);
+  if (st != MLA_OK) return st;
+  return d->act_dtype == MLA_BF16 ? MLA_OK : MLA_ERR_UNSUPPORTED;
+}
+}  // namespace
+
+MLA_EXPORT mla_status_t mla_gemm_bf16(int32_t batch, int32_t m, int32_t n, int32_t k,
+                                      const void* a, int64_t lda, int64_t stride_a,
+                                      const void* b, int64_t ldb, int64_t stride_b, void* c,
+                                      int32_t c_dtype, int64_t ldc, int64_t stride_c,
+                                      void* stream) {
+  if (batch < 0 || m < 0 || n < 0 || k < 0 || k % 8 != 0) return MLA_ERR_BAD_SHAPE;
+  if (batch > 65535) return MLA_ERR_BAD_SHAPE;
+  if (c_dtype != MLA_F32 && c_dtype != MLA_BF16) return MLA_ERR_BAD_DTYPE;
+  if (batch == 0 || m == 0 || n == 0) return MLA_OK;
+  if (!a || !b || !c) return MLA_ERR_NULL_POINTER;
+  if (lda < k || ldb < k || ldc < n || lda % 8 != 0 || ldb % 8 != 0) return MLA_ERR_BAD_SHAPE;
+  if (stride_a < 0 || stride_b < 0 || stride_c < 0) return MLA_ERR_BAD_SHAPE;
+  if (!aligned16(a) || !aligned16(b) || ((uintptr_t)c & 3u) != 0) return MLA_ERR_MISALIGNED;
+  return gemm(batch, m, n, k, a, lda, stride_a, b, ldb, stride_b, c, c_dtype == MLA_F32, ldc,
+              stride_c, reinterpret_cast<hipStream_t>(stream));
+}
+
+MLA_EXPORT mla_status_t mla_absorb_weights_workspace_size(const mla_dims_t* dims, int32_t d_cq,
+                                                          size_t* bytes) {
+  mla_status_t st = check_bf16_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!bytes) return MLA_ERR_NULL_POINTER;
+  if (d_cq < 8 || d_cq % 8 != 0) return MLA_ERR_BAD_SHAPE;
+  const size_t H = (size_t)dims->n_heads;
+  const size_t q = align_up(H * dims->d_nope * (dims->d_latent + (size_t)d_cq) * 2, 256);
+  const size_t o = align_up(H * dims->d_v * (size_t)dims->d_latent * 2, 256);
+  *bytes = q > o ? q : o;
+  return MLA_OK;
+}
+
+MLA_EXPORT mla_status_t mla_absorb_query_weights(const mla_dims_t* dims, int32_t d_cq,
+                                                 const void* w_uq, const void* w_uk,
+                                                 void* w_q_absorbed, void* workspace,
+                                                 size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  mla_status_t st = mla_absorb_weights_workspace_size(dims, d_cq, &need);
+  if (st != MLA_OK) return st;
+  if (!w_uq || !w_uk || !w_q_absorbed || !workspace) return MLA_ERR_NULL_POINTER;
+  if (!aligned16(w_uq) || !aligned16(w_uk) || !aligned16(w_q_absorbed) || !aligned16(workspace))
+    return MLA_ERR_MISALIGNED;
+  if (workspace_bytes < need) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (dims->d_nope % 8 != 0) return MLA_ERR_UNSUPPORTED;
+  const int H = dims->n_heads, dn = dims->d_nope, dc = dims->d_latent;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  void* uk_t = ws;                                        // [H, d_c, d_nope]
+  void* uq_t = ws + (size_t)H * dc * dn * 2;              // [H, d_cq, d_nope]
+  if ((st = transpose(H, dn, dc, w_uk, uk_t, s)) != MLA_OK) return st;
+  if ((st = transpose(H, dn, d_cq, w_uq, uq_t, s)) != MLA_OK) return st;
+  // W~_h[c, q] = sum_n W_UK_h^T[c, n] W_UQ_h^T[q, n]
+  return gemm(H, dc, d_cq, dn, uk_t, dn, (int64_t)dc * dn, uq_t, dn, (int64_t)d_cq * dn,
+              w_q_absorbed, 0, d_cq, (int64_t)dc * d_cq, s);
+}
+
+MLA_EXPORT mla_status_t mla_absorb_output_weights(const mla_dims_t* dims, int32_t d_model,
+                                                  const void* w_o, const void* w_uv,
+                                                  void* w_o_absorbed, void* workspace,
+                                                  size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  mla_status_t st = mla_absorb_weights_workspace_size(dims, 8, &need);
+  if (st != MLA_OK) return st;
+  if (d_model < 1) return MLA_ERR_BAD_SHAPE;
+  if (!w_o || !w_uv || !w_o_absorbed || !workspace) return MLA_ERR_NULL_POINTER;
+  if (!aligned16(w_o) || !aligned16(w_uv) || !aligned16(w_o_absorbed) || !aligned16(workspace))
+    return MLA_ERR_MISALIGNED;
+  const int H = dims->n_heads, dv = dims->d_v, dc = dims->d_latent;
+  if (dv % 8 != 0) return MLA_ERR_UNSUPPORTED;
+  if (workspace_bytes < align_up((size_t)H * dv * dc * 2, 256)) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* uv_t = workspace;                                 // [H, d_c, d_v]
+  if ((st = transpose(H, dv, dc, w_uv, uv_t, s)) != MLA_OK) return st;
+  // W~O[m, h d_c + c] = sum_v W_O[m, h d_v + v] W_UV_h^T[c, v]
+  return gemm(H, d_model, dc, dv, w_o, (int64_t)H * dv, dv, uv_t, dv, (int64_t)dc * dv,
+              w_o_absorbed, 0, (int64_t)H * dc, dc, s);
+}
+
+MLA_EXPORT mla_status_t mla_query_from_latent(const mla_dims_t* dims, int32_t batch,
+                                              int32_t q_len, int32_t d_cq, const void* c_q,
+                                              const void* w_q_absorbed, const void* w_qr,
+                                              const int32_t* seqlens, void* q_latent,
+                                              void* q_pe, void* stream) {
+  mla_status_t st = check_bf16_dims(dims);
+  if (st != MLA_OK) return st;
+  if (dims->latent_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if ((st = check_batch(batch, q_len)) != MLA_OK) return st;
+  if (d_cq < 8 || d_cq % 8 != 0) return MLA_ERR_BAD_SHAPE;
+  if (!c_q || !w_q_absorbed || !w_qr || !seqlens || !q_latent || !q_pe)
+    return MLA_ERR_NULL_POINTER;
+  if (!aligned16(c_q) || !aligned16(w_q_absorbed) || !aligned16(w_qr) || !aligned16(seqlens) ||
+      !aligned16(q_latent) || !aligned16(q_pe))
+    return MLA_ERR_MISALIGNED;
+  if (batch == 0) return MLA_OK;
+  const int H = dims->n_heads, dc = dims->d_latent, dr = dims->d_rope;
+  const int T = batch * q_len;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // q~[t, h, :] = W~_h c^Q_t: batch over heads, c^Q shared (stride 0)
+  if ((st = gemm(H, T, dc, d_cq, c_q, d_cq, 0, w_q_absorbed, d_cq, (int64_t)dc * d_cq, q_latent,
+                 0, (int64_t)H * dc, dc, s)) != MLA_OK)
+    return st;
+  // q^R = W_QR c^Q into q_pe, then rotated in place
+  if ((st = gemm(1, T, H * dr, d_cq, c_q, d_cq, 0, w_qr, d_cq, 0, q_pe, 0, (int64_t)H * dr, 0,
+                 s)) != MLA_OK)
+    return st;
+  mla::RopeArgs r;
+  r.src = q_pe; r.dst = q_pe; r.seqlens = seqlens;
+  r.batch = batch; r.q_len = q_len; r.n_heads = H; r.d_rope = dr; r.rope_base = dims->rope_base;
+  return launch_status(mla::launch_rope_query(r, s));
+}

@@ -85,4 +85,48 @@ struct ValidateArgs {
 
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
 
+struct GemmArgs {            // C[b] = A[b] B[b]^T, bf16 in, fp32 accumulate
+  const void* a;             // [batch][m][lda] bf16 (k contiguous)
+  const void* b;             // [batch][n][ldb] bf16 (k contiguous)
+  void* c;                   // [batch][m][ldc] bf16 or f32
+  int64_t lda, ldb, ldc, stride_a, stride_b, stride_c;   // elements
+  int32_t batch, m, n, k, c_f32;
+};
+hipError_t launch_gemm_nt(const GemmArgs& g, hipStream_t s);
+
+struct TransposeArgs {       // dst[b][c][r] = src[b][r][c], 16-bit elements
+  const void* src;
+  void* dst;
+  int32_t batch, rows, cols;
+};
+hipError_t launch_transpose(const TransposeArgs& t, hipStream_t s);
+
+struct RopeArgs {            // q_pe = RoPE(q_rope) at pos = seqlens[b] - q_len + j
+  const void* src;           // [batch, q_len, H, d_rope] bf16
+  void* dst;                 // same shape (may equal src)
+  const int32_t* seqlens;
+  int32_t batch, q_len, n_heads, d_rope;
+  float rope_base;
+};
+hipError_t launch_rope_query(const RopeArgs& r, hipStream_t s);
+
+struct PrefillArgs {
+  const void* q_nope;        // [batch, q_len, H, 128] bf16
+  const void* q_rope;        // [batch, q_len, H, 64] bf16, not rotated
+  const void* kv_lat;        // [num_pages, 64, 512] bf16
+  const void* kv_rope;       // [num_pages, 64, 64] bf16
+  const int32_t* block_table;
+  const int32_t* seqlens;
+  const void* w_uk;          // [H, 128, 512] bf16
+  const void* w_uv;          // [H, 128, 512] bf16
+  void* kexp;                // workspace [batch, H, lpad, 128] bf16: K^C
+  void* vexp;                // workspace [batch, H, lpad, 128] bf16: V
+  void* out;                 // [batch, q_len, H, 128] bf16
+  float* lse;                // [batch, q_len, H] or null
+  int32_t batch, q_len, n_heads, max_pages, lpad;
+  float scale_log2, rope_base;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
 }  // namespace mla

@@ -1,0 +1,370 @@
+// Non-absorbed MLA attention for many query tokens per sequence (chunked
+// prefill, multi-token verification), gfx950, bf16.
+//
+// The same attention as the decode path, in the other of the two
+// functionally equivalent forms ("Related papers: SnapMLA: Efficient
+// Long-Context MLA Decoding via H…", the abstract on two kernel formulations
+// of MLA; "Multi-Head Latent Attention: Scaling LLM Serving Throughput via
+// Low-Rank KV Compression", section "Empirical Gains": keys and values come
+// from the cached latent through W^UK and W^UV):
+//   K^C[t, h] = W_UK[h] c_t,  V[t, h] = W_UV[h] c_t            (expand_kv_kernel)
+//   s[j, t]   = scale ( q^C[j, h] . K^C[t, h] + R(pos_j) q^R[j, h] . k^R_t )
+//   out[j, h] = sum_t softmax_t(s) V[t, h]   (causal: t <= pos_j)   (attn_kernel)
+// Absorbing W_UK into the query costs 2 (d_c + d_R + d_c) flops per key and
+// query row; expanding costs 2 d_c (d_nope + d_v) per key and head once, then
+// 2 (d_nope + d_R + d_v) per key and query row, so with many query rows per
+// sequence the expanded form does far less arithmetic.
+//
+// The expansion is a GEMM per sequence: [L_b x 512] (latent rows gathered
+// through the block table) times [512 x 2 * 128 * n_heads] (the rows of W_UK
+// and W_UV), on v_mfma_f32_32x32x16_bf16, written to the workspace as bf16
+// K^C and V [B, H, L_pad, 128].  Expanding per key tile inside the attention
+// kernel instead would stream W_UK[h] and W_UV[h] (256 KiB per head) through
+// every workgroup for every tile, four times the tile's own bytes.
+//
+// The attention is flash attention with online softmax (running maximum and
+// output rescale) per workgroup of 128 query rows of one (sequence, head):
+// wave w owns rows 32w .. 32w+31.  S^T = K Q^T on 32x32x16 MFMAs (K rows
+// from LDS, Q^T from registers), so each lane holds one query row and 16
+// keys per 32-key block; O^T += V^T P^T with P^T straight from the score
+// registers and V^T read with the LDS transpose read in the same key order.
+#include "mla_common.hpp"
+#include "mla_internal.hpp"
+
+namespace mla {
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+__device__ __forceinline__ f32x16 mfma32(u16x8 a, u16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+constexpr int D_LAT = 512;
+constexpr int D_NOPE = 128;
+constexpr int D_V = 128;
+constexpr int D_ROPE = 64;
+
+// ---------------------------------------------------------------------------
+// expansion GEMM: workgroup = (128 tokens of sequence b, 128 output columns =
+// one half (K^C or V) of one head); wave w computes rows 64 (w >> 1) .. +63
+// and columns 64 (w & 1) .. +63 as 2 x 2 blocks of 32 x 32
+constexpr int EX_M = 128, EX_N = 128, EX_K = 64;   // tile and k-chunk
+constexpr int EX_PITCH = EX_K * 2 + 16;            // LDS bytes per row (16 B pad)
+constexpr int EX_TILE = EX_M * EX_PITCH;
+
+__global__ __launch_bounds__(256, 2) void expand_kv_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][EX_TILE];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][EX_TILE];
+  const int b = blockIdx.z;
+  const int len = a.seqlens[b];
+  const int t0 = blockIdx.x * EX_M;
+  if (t0 >= len) return;
+  const int h = blockIdx.y >> 1, part = blockIdx.y & 1;   // part 0: K^C, 1: V
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hh = lane >> 5, lc = lane & 31;
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+  const uint8_t* lat = (const uint8_t*)a.kv_lat;
+  const uint8_t* wmat = (const uint8_t*)(part ? a.w_uv : a.w_uk) + (int64_t)h * 128 * D_LAT * 2;
+
+  // this thread's 4 latent chunks and 4 weight chunks of each k-chunk:
+  // row = idx >> 3, 16-byte piece = idx & 7, idx = tid + 256 e
+  const uint8_t* arow[4];
+  const uint8_t* brow[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int idx = tid + 256 * e, row = idx >> 3, pc = idx & 7;
+    const int t = min(t0 + row, len - 1);     // rows past the end: any valid row
+    const int page = bt_row[t / kPage];
+    arow[e] = lat + ((int64_t)page * kPage + (t % kPage)) * (D_LAT * 2) + pc * 16;
+    brow[e] = wmat + (int64_t)row * (D_LAT * 2) + pc * 16;
+  }
+  u32x4 ra[4], rb[4];
+  auto load = [&](int kc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ra[e] = *(const u32x4*)(arow[e] + kc * EX_K * 2);
+      rb[e] = *(const u32x4*)(brow[e] + kc * EX_K * 2);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 256 * e, row = idx >> 3, pc = idx & 7;
+      *(u32x4*)(&s_a[buf][row * EX_PITCH + pc * 16]) = ra[e];
+      *(u32x4*)(&s_b[buf][row * EX_PITCH + pc * 16]) = rb[e];
+    }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  const int mrow = 64 * (w >> 1), ncol = 64 * (w & 1);
+  load(0);
+  store(0);
+  __syncthreads();
+  constexpr int NKC = D_LAT / EX_K;
+  for (int kc = 0; kc < NKC; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < NKC) load(kc + 1);
+#pragma unroll
+    for (int ks = 0; ks < EX_K / 16; ++ks) {
+      u16x8 av[2], bv[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        av[i] = *(const u16x8*)(&s_a[buf][(mrow + 32 * i + lc) * EX_PITCH + (ks * 16 + 8 * hh) * 2]);
+        bv[i] = *(const u16x8*)(&s_b[buf][(ncol + 32 * i + lc) * EX_PITCH + (ks * 16 + 8 * hh) * 2]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(av[i], bv[j], acc[i][j]);
+    }
+    if (kc + 1 < NKC) {
+      store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  // lane holds rows 8(r >> 2) + 4hh + (r & 3) of each 32-row block, column lc
+  uint16_t* dst = (uint16_t*)(part ? a.vexp : a.kexp) + ((int64_t)b * a.n_heads + h) * a.lpad * 128;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = t0 + mrow + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (t < len) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float v = acc[i][j][r];
+          dst[(int64_t)t * 128 + ncol + 32 * j + lc] =
+              (uint16_t)(__builtin_bit_cast(uint32_t, pack_bf16x2(v, 0.f)) & 0xffffu);
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// attention: workgroup = (128 query rows of sequence b, head h)
+constexpr int QB = 128;                  // query rows per workgroup
+constexpr int KT = 64;                   // keys per tile (one cache page)
+constexpr int K_PITCH = D_NOPE * 2 + 16; // 272: conflict-free 16-byte row reads
+constexpr int R_PITCH = D_ROPE * 2 + 16; // 144
+constexpr int V_PITCH = D_V * 2 + 64;    // 320: conflict-free transpose reads
+constexpr int K_OFF = 0;
+constexpr int R_OFF = KT * K_PITCH;
+constexpr int V_OFF = R_OFF + KT * R_PITCH;
+constexpr int STAGE = V_OFF + KT * V_PITCH;
+constexpr int KS_N = D_NOPE / 16;        // 8 score k-steps over q^C
+constexpr int KS = KS_N + D_ROPE / 16;   // 12
+
+__global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][STAGE];
+  const int b = blockIdx.z, h = blockIdx.y;
+  const int j0 = blockIdx.x * QB;
+  const int len = a.seqlens[b];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hh = lane >> 5, lc = lane & 31;
+  const int H = a.n_heads;
+  // the lane's query row (j >= q_len: a padding row, masked throughout)
+  const int j = j0 + 32 * w + lc;
+  const bool row_ok = j < a.q_len;
+  const int jr = row_ok ? j : 0;
+  const int pos = len - a.q_len + j;         // the row sees keys t <= pos
+  const int lim = row_ok ? min(pos + 1, len) : 0;
+  // keys the workgroup needs: up to the last valid row's position
+  const int jmax = min(j0 + QB, a.q_len) - 1;
+  const int kend = max(0, min(len, len - a.q_len + jmax + 1));
+  const int ntiles = (kend + KT - 1) / KT;
+
+  // Q^T operand: dims 16ks + 8hh .. +7 of the lane's row; q^R rotated in fp32
+  u16x8 q[KS];
+  {
+    const int64_t qrow = ((int64_t)b * a.q_len + jr) * H + h;
+    const uint16_t* qn = (const uint16_t*)a.q_nope + qrow * D_NOPE;
+    const uint16_t* qr = (const uint16_t*)a.q_rope + qrow * D_ROPE;
+#pragma unroll
+    for (int ks = 0; ks < KS_N; ++ks) q[ks] = *(const u16x8*)(qn + ks * 16 + hh * 8);
+    const int p = max(pos, 0);
+#pragma unroll
+    for (int ks = KS_N; ks < KS; ++ks) {
+      const int d0 = (ks - KS_N) * 16 + hh * 8;
+      const u16x8 x = *(const u16x8*)(qr + d0);
+      u16x8 y;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        float y0, y1;
+        rope_pair(bf16_bits_to_f32(x[e]), bf16_bits_to_f32(x[e + 1]), p,
+                  rope_theta((d0 + e) / 2, D_ROPE, a.rope_base), y0, y1);
+        const uint32_t pr = pack_bf16x2(y0, y1);
+        y[e] = (uint16_t)(pr & 0xffffu);
+        y[e + 1] = (uint16_t)(pr >> 16);
+      }
+      q[ks] = y;
+    }
+  }
+
+  // tile loads (register staged): K^C and V 4 pieces each, k^R 2 pieces
+  const uint8_t* kx = (const uint8_t*)a.kexp + ((int64_t)b * H + h) * a.lpad * 256;
+  const uint8_t* vx = (const uint8_t*)a.vexp + ((int64_t)b * H + h) * a.lpad * 256;
+  const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
+  u32x4 rk[4], rv[4], rr[2];
+  auto load = [&](int kt) {
+    const int t0 = kt * KT;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 256 * e, row = idx >> 4, pc = idx & 15;
+      const int t = min(t0 + row, len - 1);
+      rk[e] = *(const u32x4*)(kx + (int64_t)t * 256 + pc * 16);
+      rv[e] = *(const u32x4*)(vx + (int64_t)t * 256 + pc * 16);
+    }
+    const int page = bt_row[t0 / kPage];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int idx = tid + 256 * e, row = idx >> 3, pc = idx & 7;
+      const int t = min(t0 + row, len - 1);
+      const int pg = (t / kPage == t0 / kPage) ? page : bt_row[t / kPage];
+      rr[e] = *(const u32x4*)((const uint8_t*)a.kv_rope +
+                              ((int64_t)pg * kPage + (t % kPage)) * (D_ROPE * 2) + pc * 16);
+    }
+  };
+  auto store = [&](int st) {
+    uint8_t* s = s_kv[st];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 256 * e, row = idx >> 4, pc = idx & 15;
+      *(u32x4*)(s + K_OFF + row * K_PITCH + pc * 16) = rk[e];
+      *(u32x4*)(s + V_OFF + row * V_PITCH + pc * 16) = rv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int idx = tid + 256 * e, row = idx >> 3, pc = idx & 7;
+      *(u32x4*)(s + R_OFF + row * R_PITCH + pc * 16) = rr[e];
+    }
+  };
+
+  f32x16 o[D_V / 32];
+#pragma unroll
+  for (int db = 0; db < D_V / 32; ++db) o[db] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+  const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+
+  if (ntiles > 0) {
+    load(0);
+    store(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int st = kt & 1;
+    if (kt + 1 < ntiles) load(kt + 1);
+    const uint8_t* s = s_kv[st];
+    const int t0 = kt * KT;
+    // scores of the two 32-key blocks
+    f32x16 sc[2];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk) {
+      sc[bk] = f32x16{};
+      const int key = 32 * bk + lc;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u16x8 kv;
+        if (ks < KS_N)
+          kv = *(const u16x8*)(s + K_OFF + key * K_PITCH + (ks * 16 + hh * 8) * 2);
+        else
+          kv = *(const u16x8*)(s + R_OFF + key * R_PITCH + ((ks - KS_N) * 16 + hh * 8) * 2);
+        sc[bk] = mfma32(kv, q[ks], sc[bk]);
+      }
+    }
+    // online softmax (log2 units); lane: row lc, keys 32bk + 8(i >> 2) + 4hh + (i & 3)
+    float x[2][16];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = t0 + 32 * bk + 8 * (i >> 2) + 4 * hh + (i & 3);
+        x[bk][i] = t < lim ? sc[bk][i] * a.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, x[bk][i]);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(m, mt);
+    if (mn > m) {
+      // a row whose maximum grew rescales its output (m = -inf: nothing yet)
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D_V / 32; ++db) o[db] *= alpha;
+      m = mn;
+    }
+    const float msub = m == -INFINITY ? 0.f : m;
+    u16x8 pk[2][2];
+    float psum = 0.f;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int i = 8 * kb + 2 * c;
+          w4[c] = pack_bf16x2(fast_exp2(x[bk][i] - msub), fast_exp2(x[bk][i + 1] - msub));
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[c]), one2, psum,
+                                                 false);
+        }
+        pk[bk][kb] = __builtin_bit_cast(u16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
+      }
+    l += psum;
+    // O^T += V^T P^T: k-step (bk, kb) covers keys 32bk + 16kb + {4hh + r, 8 + 4hh + r}
+    const int g1 = (lane >> 4) & 1, r = (lane & 15) >> 2, qd = lane & 3;
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = 32 * bk + 16 * kb + 4 * hh + r;
+#pragma unroll
+        for (int db = 0; db < D_V / 32; ++db) {
+          const uint8_t* p = s + V_OFF + key * V_PITCH + (32 * db + 16 * g1 + 4 * qd) * 2;
+          const u16x4 lo4 = lds_read_tr16((const MLA_LDS uint8_t*)(p));
+          const u16x4 hi4 = lds_read_tr16((const MLA_LDS uint8_t*)(p + 8 * V_PITCH));
+          const u16x8 va = u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          o[db] = mfma32(va, pk[bk][kb], o[db]);
+        }
+      }
+    // (stage st ^ 1 was last read in the previous iteration, which every
+    // wave left at the barrier below)
+    if (kt + 1 < ntiles) {
+      store(st ^ 1);
+      __syncthreads();
+    }
+  }
+  // normalise and store: lane holds row lc, dims 32db + 8(i >> 2) + 4hh + (i & 3)
+  const float lsum = l + __shfl_xor(l, 32, 64);
+  if (!row_ok) return;
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  uint16_t* out = (uint16_t*)a.out + (((int64_t)b * a.q_len + j) * H + h) * D_V;
+#pragma unroll
+  for (int db = 0; db < D_V / 32; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *(u32x2*)(out + 32 * db + 8 * g + 4 * hh) =
+          u32x2{pack_bf16x2(o[db][4 * g] * inv, o[db][4 * g + 1] * inv),
+                pack_bf16x2(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv)};
+  if (a.lse != nullptr && hh == 0)
+    a.lse[((int64_t)b * a.q_len + j) * H + h] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
+  const int tok_blocks = (a.lpad + EX_M - 1) / EX_M;
+  hipLaunchKernelGGL(expand_kv_kernel, dim3(tok_blocks, 2 * a.n_heads, a.batch), dim3(256), 0, s,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_kernel, dim3((a.q_len + QB - 1) / QB, a.n_heads, a.batch), dim3(256), 0,
+                     s, a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

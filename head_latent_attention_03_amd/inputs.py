@@ -96,6 +96,15 @@ def workload(n, **overrides):
     return replace(s, **overrides) if overrides else s
 
 
+def prefill_workload(**overrides):
+    """A chunked-prefill batch for the non-absorbed path: 4 sequences of 4096 cached
+    tokens whose last 1024 are the chunk being attended (DeepSeek-V3 shapes, bf16,
+    N(0,1)*0.02 as the B=64 decode workload); seed 1006."""
+    s = Spec("dsv3-bf16-prefill-b4-q1024-l4096", batch=4, q_len=1024, n_heads=128, d_c=512,
+             d_rope=64, d_nope=128, d_v=128, seqlen=4096, seed=1006)
+    return replace(s, **overrides) if overrides else s
+
+
 def _f32_to_bf16_bits(x):
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)

@@ -116,3 +116,31 @@ class DeviceBatch:
         self.absorb(stream)
         self.decode(stream=stream)
         self.combine(with_uv=with_uv, stream=stream)
+
+
+def prefill_step(wl, device="cuda:0", stream=None):
+    """Upload a workload and run mla_prefill_paged on it (the non-absorbed form):
+    returns (out [B, q_len, H, d_v], lse [B, q_len, H]) on the device."""
+    s = wl.spec
+    dims = dims_of(s)
+    dev = torch.device(device)
+    Bn, S, H = s.batch, s.q_len, s.n_heads
+    act = dims.act_torch
+    t = dict(
+        q_nope=_to_device(wl.q_nope, s.act_dtype, dev),
+        q_rope=_to_device(wl.q_rope, s.act_dtype, dev),
+        kv_latent=_to_device(wl.kv_latent, s.latent_dtype, dev),
+        kv_rope=_to_device(wl.kv_rope, s.act_dtype, dev),
+        block_table=_to_device(wl.block_table, "i32", dev),
+        seqlens=_to_device(wl.seqlens, "i32", dev),
+        w_uk=_to_device(wl.w_uk, s.act_dtype, dev),
+        w_uv=_to_device(wl.w_uv, s.act_dtype, dev),
+    )
+    ws = torch.empty(max(B.mla_prefill_workspace_size(dims, Bn, wl.max_seqlen), 16),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((Bn, S, H, s.d_v), dtype=act, device=dev)
+    lse = torch.empty((Bn, S, H), dtype=torch.float32, device=dev)
+    B.mla_prefill_paged(dims, t["q_nope"], t["q_rope"], t["kv_latent"], t["kv_rope"],
+                        t["block_table"], t["seqlens"], wl.max_seqlen, t["w_uk"], t["w_uv"], ws,
+                        out, lse, stream=stream)
+    return out, lse

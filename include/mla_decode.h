@@ -267,6 +267,107 @@ mla_status_t mla_decode_noalloc(const mla_dims_t* dims, int32_t batch, int32_t q
                                 const int32_t* seqlens, int32_t max_seqlen, const void* w_uv,
                                 void* out, float* lse, void* stream);
 
+/*
+ * Many query tokens per sequence (chunked prefill, verification of several
+ * drafted tokens) in the NON-absorbed form: the other of the two
+ * functionally equivalent MLA kernel formulations ("Related papers: SnapMLA:
+ * Efficient Long-Context MLA Decoding via H…", scifaro.com, the abstract on
+ * two formulations).  Per head, the content keys and values are expanded
+ * from the cached latent, K^C_t = W_UK[h] c_t and V_t = W_UV[h] c_t ("Multi-
+ * Head Latent Attention: Scaling LLM Serving Throughput via Low-Rank KV
+ * Compression", "Empirical Gains"), then ordinary causal attention runs:
+ *     s = softmax_scale * ( q^C . K^C_t + R(pos_j) q^R . k^R_t ),
+ *     out[b, j, h] = sum_{t <= pos_j} softmax(s)_t V_t,
+ * with pos_j = seqlens[b] - q_len + j (the chunk's tokens are already in the
+ * cache).  The result equals mla_absorb_q + mla_decode_paged(causal) +
+ * mla_combine(w_uv) up to rounding; with many query rows it does less
+ * arithmetic (2 d_c (d_nope + d_v) per key and head once, then
+ * 2 (d_nope + d_R + d_v) per key and row).
+ *   q_nope [batch, q_len, n_heads, d_nope] act; q_rope [batch, q_len,
+ *          n_heads, d_rope] act, not rotated (rotated here in fp32)
+ *   kv_latent, kv_rope, num_pages, block_table, max_pages_per_seq, seqlens,
+ *          max_seqlen: the paged cache, as for mla_decode_paged
+ *   w_uk, w_uv [n_heads, 128, d_latent] act
+ *   workspace  >= mla_prefill_workspace_size() bytes: the expanded K^C and V
+ *          [batch, n_heads, ceil(max_seqlen / 64) * 64, 128] bf16 each
+ *   out   [batch, q_len, n_heads, d_v] act;  lse [batch, q_len, n_heads] f32
+ *          natural log, or NULL.  A row with no visible key outputs zeros and
+ *          LSE = -inf.
+ * Supported: act BF16 and latent BF16 at the decode path's dims;
+ * 1 <= q_len <= 65536.  Errors, preconditions and MLA_VALIDATE as for
+ * mla_decode_paged.
+ */
+mla_status_t mla_prefill_workspace_size(const mla_dims_t* dims, int32_t batch,
+                                        int32_t max_seqlen, size_t* bytes);
+mla_status_t mla_prefill_paged(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                               const void* q_nope, const void* q_rope, const void* kv_latent,
+                               const void* kv_rope, int32_t num_pages,
+                               const int32_t* block_table, int32_t max_pages_per_seq,
+                               const int32_t* seqlens, int32_t max_seqlen, const void* w_uk,
+                               const void* w_uv, void* workspace, size_t workspace_bytes,
+                               void* out, float* lse, void* stream);
+
+/*
+ * Dense products around the attention: the latent down-projections of the
+ * hidden state ("Multi-Head Latent Attention – Latent KV-Cache (DeepSeek
+ * v3)", eeumee.net, "Operation Flow", step 1: c^Q, c^KV from h), the query
+ * up-projection (step 2) and the weight-level absorption of W^UK into the
+ * query weights and of W^UV into the output projection W^O ("Multi-Head
+ * Latent Attention: Scaling LLM Serving Throughput via Low-Rank KV
+ * Compression", "Empirical Gains", the paragraph on absorption).
+ *
+ * mla_gemm_bf16: C[b] = A[b] B[b]^T for b < batch, bf16 inputs, fp32
+ *   accumulation.  A [m, lda] and B [n, ldb] are row-major with the k
+ *   dimension contiguous (lda, ldb >= k, multiples of 8; k a multiple of 8);
+ *   C [m, ldc] row-major in c_dtype (MLA_BF16, rounded to nearest even, or
+ *   MLA_F32); stride_* in elements between batch entries (0 shares an
+ *   operand).  A and B 16-byte aligned, C 4-byte aligned.  A down-projection
+ *   c = W^D h of T tokens is mla_gemm_bf16(1, T, d_out, d_model, h, d_model,
+ *   0, W^D, d_model, 0, c, ...).
+ */
+mla_status_t mla_gemm_bf16(int32_t batch, int32_t m, int32_t n, int32_t k, const void* a,
+                           int64_t lda, int64_t stride_a, const void* b, int64_t ldb,
+                           int64_t stride_b, void* c, int32_t c_dtype, int64_t ldc,
+                           int64_t stride_c, void* stream);
+
+/*
+ * Weight-level absorption (bf16 activations), done once per set of weights:
+ *   mla_absorb_query_weights:  W~[h] = W_UK[h]^T W_UQ[h]
+ *       w_uq [n_heads, d_nope, d_cq], w_uk [n_heads, d_nope, d_latent]
+ *       -> w_q_absorbed [n_heads, d_latent, d_cq] (bf16), so that the absorbed
+ *       query of a token is q~[h] = W~[h] c^Q (mla_query_from_latent);
+ *   mla_absorb_output_weights: W~O[:, h d_latent + c] = sum_v W_O[:, h d_v + v] W_UV[h][v][c]
+ *       w_o [d_model, n_heads d_v], w_uv [n_heads, d_v, d_latent]
+ *       -> w_o_absorbed [d_model, n_heads d_latent] (bf16), so that the layer
+ *       output is y = W~O [o~_1; ...; o~_H] from the latent outputs o~ that
+ *       mla_combine writes with w_uv = NULL (one mla_gemm_bf16).
+ * workspace: >= mla_absorb_weights_workspace_size() bytes (transposed weight
+ * copies).  d_cq a multiple of 8.
+ */
+mla_status_t mla_absorb_weights_workspace_size(const mla_dims_t* dims, int32_t d_cq,
+                                               size_t* bytes);
+mla_status_t mla_absorb_query_weights(const mla_dims_t* dims, int32_t d_cq, const void* w_uq,
+                                      const void* w_uk, void* w_q_absorbed, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+mla_status_t mla_absorb_output_weights(const mla_dims_t* dims, int32_t d_model, const void* w_o,
+                                       const void* w_uv, void* w_o_absorbed, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
+ * The decode query from the query latent through absorbed weights (in place
+ * of mla_absorb_q when W_UK has been folded into the query weights):
+ *   q_latent[b, j, h] = W~[h] c_q[b, j]          (W~ from mla_absorb_query_weights)
+ *   q_pe[b, j, h]     = R(pos_j) (W_QR c_q[b, j])[h d_rope ..]   (fp32 rotation,
+ *                       pos_j = seqlens[b] - q_len + j, as mla_absorb_q)
+ *   c_q [batch, q_len, d_cq] bf16; w_q_absorbed [n_heads, d_latent, d_cq];
+ *   w_qr [n_heads d_rope, d_cq]; q_latent [batch, q_len, n_heads, d_latent];
+ *   q_pe [batch, q_len, n_heads, d_rope].  BF16 latents only.
+ */
+mla_status_t mla_query_from_latent(const mla_dims_t* dims, int32_t batch, int32_t q_len,
+                                   int32_t d_cq, const void* c_q, const void* w_q_absorbed,
+                                   const void* w_qr, const int32_t* seqlens, void* q_latent,
+                                   void* q_pe, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(mla_status_t status);
 

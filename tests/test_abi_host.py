@@ -150,3 +150,63 @@ def test_validate_paged_host_finds_each_broken_precondition(lib):
     code, _ = B.mla_validate_paged_host(d, num_pages, good_t[:, :3], good_l, max_seqlen)
     assert code == 2
 
+
+
+def test_prefill_argument_checks(lib):
+    """mla_prefill_paged answers from the host checks (bf16 only; q_len up to 65536;
+    table wide enough for max_seqlen; workspace size) before any device call."""
+    d = _dims()
+    nb = ctypes.c_size_t(0)
+    assert lib.mla_prefill_workspace_size(ctypes.byref(d), 2, 100, ctypes.byref(nb)) == 0
+    # K^C and V rows, padded to whole pages: 2 x B x H x 128 x 128 x 2 bytes
+    assert nb.value == 2 * 2 * 128 * 128 * 128 * 2
+    assert lib.mla_prefill_workspace_size(ctypes.byref(_dims(latent_dtype="e4m3")), 2, 100,
+                                          ctypes.byref(nb)) == 6
+    call = lambda **kw: lib.mla_prefill_paged(
+        ctypes.byref(kw.get("dims", d)), 2, kw.get("q_len", 100), kw.get("qn", A16), A16, A16,
+        A16, 10, A16, kw.get("max_pages", 4), A16, kw.get("max_seqlen", 100), A16, A16,
+        kw.get("ws", A16), kw.get("ws_bytes", 1 << 30), kw.get("out", A16), NULL, NULL)
+    assert call(qn=NULL) == 1
+    assert call(out=NULL) == 1
+    assert call(ws=NULL) == 1
+    assert call(q_len=0) == 2 and call(q_len=65537) == 2
+    assert call(max_pages=1) == 2
+    assert call(qn=A8) == 4
+    assert call(ws_bytes=1024) == 5
+    assert call(dims=_dims(act_dtype="f32", latent_dtype="f32", d_latent=64, d_rope=16,
+                           d_nope=32, d_v=32)) == 6
+
+
+def test_gemm_and_weight_absorption_argument_checks(lib):
+    g = lambda **kw: lib.mla_gemm_bf16(
+        kw.get("batch", 1), kw.get("m", 16), kw.get("n", 16), kw.get("k", 64), kw.get("a", A16),
+        kw.get("lda", 64), 0, A16, kw.get("ldb", 64), 0, kw.get("c", A16), kw.get("cd", 1),
+        kw.get("ldc", 16), 0, NULL)
+    assert g(k=12) == 2                                            # k not a multiple of 8
+    assert g(lda=32) == 2                                          # lda < k
+    assert g(ldc=8) == 2                                           # ldc < n
+    assert g(cd=2) == 3                                            # fp8 output
+    assert g(a=NULL) == 1
+    assert g(a=A8) == 4
+    assert g(m=0) == 0 and g(batch=0) == 0                         # empty: nothing launched
+    assert g(batch=70000) == 2
+    d = _dims()
+    nb = ctypes.c_size_t(0)
+    assert lib.mla_absorb_weights_workspace_size(ctypes.byref(d), 1536, ctypes.byref(nb)) == 0
+    assert nb.value >= 128 * 128 * (512 + 1536) * 2
+    assert lib.mla_absorb_weights_workspace_size(ctypes.byref(d), 100, ctypes.byref(nb)) == 2
+    aq = lambda **kw: lib.mla_absorb_query_weights(
+        ctypes.byref(d), 1536, kw.get("uq", A16), A16, A16, kw.get("ws", A16),
+        kw.get("ws_bytes", 1 << 30), NULL)
+    assert aq(uq=NULL) == 1
+    assert aq(ws_bytes=16) == 5
+    ao = lambda **kw: lib.mla_absorb_output_weights(
+        ctypes.byref(d), kw.get("dm", 1024), A16, A16, A16, A16, kw.get("ws_bytes", 1 << 30), NULL)
+    assert ao(dm=0) == 2
+    assert ao(ws_bytes=16) == 5
+    qf = lambda **kw: lib.mla_query_from_latent(
+        ctypes.byref(kw.get("dims", d)), 2, kw.get("q_len", 1), 1536, A16, A16, A16, A16,
+        kw.get("ql", A16), A16, NULL)
+    assert qf(ql=NULL) == 1
+    assert qf(q_len=9) == 2
+    assert qf(dims=_dims(latent_dtype="e4m3")) == 6
