@@ -110,9 +110,20 @@ def summarize_pmc(fetch_dir, write_dir, kind, workload, copy_mib, commands):
     ruler."""
     def load(d, counter):
         f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
-        if not f:
-            raise SystemExit(f"no counter_collection.csv under {d}")
-        return _pmc_rows(f[0], counter)
+        if f:
+            return _pmc_rows(f[0], counter)
+        dbs = glob.glob(os.path.join(d, "**", "*_results.db"), recursive=True)
+        if not dbs:
+            raise SystemExit(f"no counter_collection.csv or rocprofv3 database under {d}")
+        import sqlite3
+        rows = {}
+        con = sqlite3.connect(dbs[0])
+        for name, disp, val in con.execute(
+                "select kernel_name, dispatch_id, value from counters_collection "
+                "where counter_name = ?", (counter,)):
+            rows[(name, str(disp))] = rows.get((name, str(disp)), 0.0) + float(val)
+        con.close()
+        return rows
     out = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = load(d, counter)
@@ -173,6 +184,55 @@ def summarize_trace(db_glob, out_name, title, commands):
             short = name.replace("mla::(anonymous namespace)::", "")
             fh.write(f"{short[:72]:72s} {len(v):5d} {v.mean():8.2f} {np.median(v):8.2f} "
                      f"{v.min():8.2f} {v.max():8.2f} {100 * v.sum() / total:5.1f}%\n")
+    print(open(out).read())
+
+
+def summarize_counters(db_glob, out_name, title, commands):
+    """Write per-kernel averages of every counter in rocprofv3 --pmc databases
+    (profiles/<out_name>), with the derived MFMA rate and busy fractions when
+    the MFMA counters are present.  The MOPS counters count 512-flop units and
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs."""
+    import sqlite3
+    paths = sorted(glob.glob(db_glob, recursive=True))
+    if not paths:
+        raise SystemExit(f"no rocprofv3 database matches {db_glob}")
+    per = {}
+    for path in paths:
+        con = sqlite3.connect(path)
+        for name, disp, cname, val in con.execute(
+                "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+            d = per.setdefault(name, {}).setdefault(cname, {})
+            d[disp] = d.get(disp, 0.0) + float(val)
+        con.close()
+    out = os.path.join(PROFILES, out_name)
+    with open(out, "w") as fh:
+        fh.write(f"# per-dispatch counter averages: {title}\n")
+        for c in commands:
+            fh.write(f"# command: {c}\n")
+        fh.write("# derived: mfma_flops = (MOPS_BF16 + MOPS_F8 + MOPS_F6F4) * 512; "
+                 "kernel_cycles = GRBM_GUI_ACTIVE / 8;\n"
+                 "#          mfma_busy = VALU_MFMA_BUSY_CYCLES / (BUSY_CU_CYCLES);  "
+                 "lds_conflict = LDS_BANK_CONFLICT / LDS_IDX_ACTIVE\n")
+        for name, cs in sorted(per.items()):
+            short = name.replace("mla::(anonymous namespace)::", "")
+            if "mla::" not in name:
+                continue
+            avg = {c: float(np.mean(list(v.values()))) for c, v in cs.items()}
+            n = max(len(v) for v in cs.values())
+            fh.write(f"\n{short}  ({n} dispatches)\n")
+            for c in sorted(avg):
+                fh.write(f"  {c:36s} {avg[c]:16.1f}\n")
+            mops = sum(avg.get(f"SQ_INSTS_VALU_MFMA_MOPS_{t}", 0.0) for t in ("BF16", "F8", "F6F4"))
+            if mops:
+                fh.write(f"  {'mfma_flops':36s} {mops * 512:16.4g}\n")
+            if "GRBM_GUI_ACTIVE" in avg:
+                fh.write(f"  {'kernel_cycles':36s} {avg['GRBM_GUI_ACTIVE'] / 8:16.1f}\n")
+            if avg.get("SQ_BUSY_CU_CYCLES") and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                fh.write(f"  {'mfma_busy':36s} "
+                         f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / avg['SQ_BUSY_CU_CYCLES']:16.4f}\n")
+            if avg.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in avg:
+                fh.write(f"  {'lds_conflict':36s} "
+                         f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:16.4f}\n")
     print(open(out).read())
 
 
@@ -341,6 +401,84 @@ def decode_object(cfg, launches, copy_mib=0):
     return out
 
 
+def second_pass_share(wl, cus, slack=0.75):
+    """Share of the e4m3 decode's workgroups that must run their chunk twice on
+    workload `wl`, from the exact scores (fp32 numpy on the stored values; the
+    kernel's e4m3 query moves them slightly): the plan cuts each sequence into
+    chunks of 32-token tiles (s = min(tiles, max(1, floor(G tiles / NT))) chunks
+    per sequence for G compute units); a row's reference is its largest score
+    in the chunk's first tile, and the chunk is redone when any later score of
+    any of its rows passes that reference by more than `slack` (log2 units)."""
+    spec = wl.spec
+    scale = spec.scale() * math.log2(math.e)
+    dec = lambda a, dt: (a.astype(np.uint32) << 16).view(np.float32) if dt == "bf16" else a
+    e4m3 = np.array([(-1.0 if c & 0x80 else 1.0) * ((c & 7) * 2.0 ** -9 if (c >> 3) & 15 == 0
+                     else (1 + (c & 7) / 8) * 2.0 ** (((c >> 3) & 15) - 7)) for c in range(256)],
+                    dtype=np.float32)
+    w_uk = dec(wl.w_uk, "bf16")
+    rows_groups = (spec.q_len * spec.n_heads + 127) // 128
+    tiles = [(int(L) + 31) // 32 for L in wl.seqlens]
+    nt = sum(tiles) * rows_groups
+    redo = chunks = 0
+    for b, L in enumerate(wl.seqlens):
+        L = int(L)
+        if L == 0:
+            continue
+        pages = wl.block_table[b, :(L + 63) // 64]
+        lat = e4m3[wl.kv_latent[pages].reshape(-1, spec.d_c)[:L]] \
+            * wl.kv_scale[pages].reshape(-1)[:L, None]
+        kr = dec(wl.kv_rope[pages].reshape(-1, spec.d_rope)[:L], "bf16")
+        qn = dec(wl.q_nope[b], "bf16").reshape(-1, spec.d_nope)        # [q_len H, d_nope]
+        qr = dec(wl.q_rope[b], "bf16").reshape(-1, spec.d_rope)
+        pos = L - spec.q_len + np.repeat(np.arange(spec.q_len), spec.n_heads)
+        theta = 10000.0 ** (-2.0 * np.arange(spec.d_rope // 2) / spec.d_rope)
+        ang = pos[:, None] * theta[None, :]
+        qpe = np.empty_like(qr)
+        qpe[:, 0::2] = qr[:, 0::2] * np.cos(ang) - qr[:, 1::2] * np.sin(ang)
+        qpe[:, 1::2] = qr[:, 0::2] * np.sin(ang) + qr[:, 1::2] * np.cos(ang)
+        heads = np.tile(np.arange(spec.n_heads), spec.q_len)
+        qlat = np.einsum("rn,rnc->rc", qn, w_uk[heads])
+        sc = (qlat @ lat.T + qpe @ kr.T) * scale                      # [rows, L]
+        lim = pos + 1
+        sc[np.arange(L)[None, :] >= lim[:, None]] = -np.inf
+        n_t = tiles[b]
+        s_u = min(n_t, max(1, (cus * n_t) // nt))
+        for c in range(s_u):
+            k0, k1 = c * n_t // s_u, (c + 1) * n_t // s_u
+            first = sc[:, k0 * 32:min((k0 + 1) * 32, L)].max(axis=1)
+            later = sc[:, (k0 + 1) * 32:min(k1 * 32, L)]
+            jump = later.shape[1] > 0 and bool(np.any(later.max(axis=1) > first + slack))
+            chunks += rows_groups
+            redo += rows_groups if jump else 0
+    return redo / max(chunks, 1)
+
+
+def fp8_second_pass_object(launches, cus):
+    """The e4m3 decode on the B=64 L=4096 e4m3 workload as drawn and with peaked
+    attention (N(0,1)/sqrt(dim) inputs, softmax scale 2): launch times and the
+    share of workgroups whose chunk must be run twice."""
+    import torch
+    from head_latent_attention_03_amd import inputs
+    from head_latent_attention_03_amd.runner import DeviceBatch
+    out = {}
+    for name, over in (("as_drawn", {}), ("peaked", dict(init="fan_in", softmax_scale=2.0))):
+        spec = inputs.workload(4, **over)
+        wl = inputs.make_workload(spec)
+        share = second_pass_share(wl, cus)
+        db = DeviceBatch.from_workload(wl, "cuda:0")
+        reps = replicate_cache(db)
+        db.absorb()
+        ms = time_decode(db, reps, launches)
+        out[name] = {"launch_ms": round(float(np.mean(ms)), 5),
+                     "launch_ms_median": round(float(np.median(ms)), 5),
+                     "second_pass_share_estimate": round(share, 4)}
+        del reps, db
+        torch.cuda.empty_cache()
+    out["note"] = ("share: workgroups whose chunk has a score past its first tile's row "
+                   "maximum + 0.75 (log2 units), from the exact scores")
+    return out
+
+
 def prefill_flops(spec, seqlens):
     """Algorithmic flops of the non-absorbed path: the expansion (2 d_c (d_nope + d_v)
     per cached token and head) and the causal attention (2 (d_nope + d_R + d_v) per
@@ -486,7 +624,7 @@ def cpu_baseline(wl, budget_s):
 
 
 EXTRA_WORKLOADS = {"e4m3_cache": 4, "long_context": 3, "mtp2": 5, "prefill": "prefill",
-                   "projection": "projection"}
+                   "projection": "projection", "e4m3_second_pass": "second_pass"}
 
 
 def main():
@@ -497,11 +635,14 @@ def main():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--decode-launches", type=int, default=50,
                     help="decode launches timed one by one for each roofline object")
-    ap.add_argument("--extra", default="e4m3_cache,long_context,mtp2,prefill,projection",
+    ap.add_argument("--extra", default="e4m3_cache,long_context,mtp2,prefill,projection,"
+                                       "e4m3_second_pass",
                     help="comma-separated decode-only objects for the other workloads "
                          f"({', '.join(EXTRA_WORKLOADS)}; empty: none)")
     ap.add_argument("--decode-only", type=int, default=0, metavar="N",
                     help="time only the decode of workload N (for profiling runs) and exit")
+    ap.add_argument("--object", choices=["prefill", "projection"],
+                    help="time only this extra object (for profiling runs) and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -514,7 +655,13 @@ def main():
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DB_GLOB", "OUT_NAME", "TITLE"),
                     help="write profiles/OUT_NAME from rocprofv3 --kernel-trace databases "
                          "(the --pmc-command lines are recorded) and exit")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("DB_GLOB", "OUT_NAME", "TITLE"),
+                    help="write profiles/OUT_NAME with per-kernel averages of the counters "
+                         "in rocprofv3 --pmc databases and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.pmc_command)
+        return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, args.pmc_command)
         return
@@ -534,6 +681,11 @@ def main():
     from head_latent_attention_03_amd.runner import DeviceBatch
 
     torch.cuda.set_device(0)
+    if args.object:
+        obj = (prefill_object(max(5, args.decode_launches // 5)) if args.object == "prefill"
+               else projection_object(max(10, args.decode_launches // 2)))
+        print(json.dumps(obj), flush=True)
+        return
     if args.decode_only:
         obj = decode_object(args.decode_only, args.decode_launches, args.copy_calibration_mib)
         print(json.dumps(obj), flush=True)
@@ -618,6 +770,9 @@ def main():
                 out[name] = prefill_object(max(5, args.decode_launches // 5))
             elif EXTRA_WORKLOADS[name] == "projection":
                 out[name] = projection_object(max(10, args.decode_launches // 2))
+            elif EXTRA_WORKLOADS[name] == "second_pass":
+                out[name] = fp8_second_pass_object(max(10, args.decode_launches // 2),
+                                                   torch.cuda.get_device_properties(0).multi_processor_count)
             else:
                 out[name] = decode_object(EXTRA_WORKLOADS[name], args.decode_launches)
     if args.cpu_budget > 0:
