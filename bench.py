@@ -401,14 +401,17 @@ def decode_object(cfg, launches, copy_mib=0):
     return out
 
 
-def second_pass_share(wl, cus, slack=0.75):
+def second_pass_share(wl, cus, limit=108.75):
     """Share of the e4m3 decode's workgroups that must run their chunk twice on
     workload `wl`, from the exact scores (fp32 numpy on the stored values; the
     kernel's e4m3 query moves them slightly): the plan cuts each sequence into
     chunks of 32-token tiles (s = min(tiles, max(1, floor(G tiles / NT))) chunks
-    per sequence for G compute units); a row's reference is its largest score
-    in the chunk's first tile, and the chunk is redone when any later score of
-    any of its rows passes that reference by more than `slack` (log2 units)."""
+    per sequence for G compute units).  The kernel works on v_t = s_t +
+    log2(token scale) (log2 units); a row's reference is its largest v in the
+    chunk's first tile, and the chunk is redone when any later v of any of its
+    rows passes that reference by more than `limit`: 100 for the largest
+    block exponent the kernel keeps plus the 8.75 by which a tile's largest
+    probability sits above 2^exponent."""
     spec = wl.spec
     scale = spec.scale() * math.log2(math.e)
     dec = lambda a, dt: (a.astype(np.uint32) << 16).view(np.float32) if dt == "bf16" else a
@@ -439,6 +442,7 @@ def second_pass_share(wl, cus, slack=0.75):
         heads = np.tile(np.arange(spec.n_heads), spec.q_len)
         qlat = np.einsum("rn,rnc->rc", qn, w_uk[heads])
         sc = (qlat @ lat.T + qpe @ kr.T) * scale                      # [rows, L]
+        sc = sc + np.log2(wl.kv_scale[pages].reshape(-1)[:L])[None, :]
         lim = pos + 1
         sc[np.arange(L)[None, :] >= lim[:, None]] = -np.inf
         n_t = tiles[b]
@@ -447,21 +451,24 @@ def second_pass_share(wl, cus, slack=0.75):
             k0, k1 = c * n_t // s_u, (c + 1) * n_t // s_u
             first = sc[:, k0 * 32:min((k0 + 1) * 32, L)].max(axis=1)
             later = sc[:, (k0 + 1) * 32:min(k1 * 32, L)]
-            jump = later.shape[1] > 0 and bool(np.any(later.max(axis=1) > first + slack))
+            jump = later.shape[1] > 0 and bool(np.any(later.max(axis=1) > first + limit))
             chunks += rows_groups
             redo += rows_groups if jump else 0
     return redo / max(chunks, 1)
 
 
 def fp8_second_pass_object(launches, cus):
-    """The e4m3 decode on the B=64 L=4096 e4m3 workload as drawn and with peaked
-    attention (N(0,1)/sqrt(dim) inputs, softmax scale 2): launch times and the
-    share of workgroups whose chunk must be run twice."""
+    """The e4m3 decode on the B=64 L=4096 e4m3 workload as drawn, with peaked
+    attention (N(0,1)/sqrt(dim) inputs, softmax scale 2) and with scores spread
+    over hundreds of log2 units (softmax scale 64, far past any trained
+    model's): launch times and the share of workgroups whose chunk must be run
+    twice."""
     import torch
     from head_latent_attention_03_amd import inputs
     from head_latent_attention_03_amd.runner import DeviceBatch
     out = {}
-    for name, over in (("as_drawn", {}), ("peaked", dict(init="fan_in", softmax_scale=2.0))):
+    for name, over in (("as_drawn", {}), ("peaked", dict(init="fan_in", softmax_scale=2.0)),
+                       ("extreme", dict(init="fan_in", softmax_scale=64.0))):
         spec = inputs.workload(4, **over)
         wl = inputs.make_workload(spec)
         share = second_pass_share(wl, cus)
@@ -474,8 +481,9 @@ def fp8_second_pass_object(launches, cus):
                      "second_pass_share_estimate": round(share, 4)}
         del reps, db
         torch.cuda.empty_cache()
-    out["note"] = ("share: workgroups whose chunk has a score past its first tile's row "
-                   "maximum + 0.75 (log2 units), from the exact scores")
+    out["note"] = ("share: workgroups whose chunk has a score (plus log2 of its token scale) "
+                   "more than 108.75 log2 units past its first tile's row maximum, from the "
+                   "exact scores")
     return out
 
 
@@ -641,7 +649,7 @@ def main():
                          f"({', '.join(EXTRA_WORKLOADS)}; empty: none)")
     ap.add_argument("--decode-only", type=int, default=0, metavar="N",
                     help="time only the decode of workload N (for profiling runs) and exit")
-    ap.add_argument("--object", choices=["prefill", "projection"],
+    ap.add_argument("--object", choices=["prefill", "projection", "e4m3_second_pass"],
                     help="time only this extra object (for profiling runs) and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
@@ -682,8 +690,13 @@ def main():
 
     torch.cuda.set_device(0)
     if args.object:
-        obj = (prefill_object(max(5, args.decode_launches // 5)) if args.object == "prefill"
-               else projection_object(max(10, args.decode_launches // 2)))
+        if args.object == "prefill":
+            obj = prefill_object(max(5, args.decode_launches // 5))
+        elif args.object == "projection":
+            obj = projection_object(max(10, args.decode_launches // 2))
+        else:
+            obj = fp8_second_pass_object(max(10, args.decode_launches // 2),
+                                         torch.cuda.get_device_properties(0).multi_processor_count)
         print(json.dumps(obj), flush=True)
         return
     if args.decode_only:

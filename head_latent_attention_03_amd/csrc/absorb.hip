@@ -185,8 +185,17 @@ __global__ __launch_bounds__(256, 1) void absorb_bf16_kernel(AbsorbArgs a) {
       const int ml = y * 16 + lr;
       const int m = mb * M + ml;
       const float amax = fmaxf(fmaxf(s_amax[0][ml], s_amax[1][ml]), fmaxf(s_amax[2][ml], s_amax[3][ml]));
-      const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
-      const float inv = 1.0f / sc;
+      // the row scale is the smallest power of two with amax / scale <= 448,
+      // so that the scaling itself is exact and the decode can apply it as
+      // an MFMA block-scale exponent (an all-zero row takes 1)
+      int ex = 0;
+      if (amax > 0.f) {
+        const float f = frexpf(amax * (1.0f / 448.0f), &ex);
+        if (f == 0.5f) --ex;
+        ex = min(max(ex, -126), 127);
+      }
+      const float sc = ldexpf(1.0f, ex);
+      const float inv = ldexpf(1.0f, -ex);
       if (m >= m_total) continue;
       uint8_t* o = (uint8_t*)a.q_lat + ((int64_t)m * a.n_heads + h) * AB_N;
 #pragma unroll

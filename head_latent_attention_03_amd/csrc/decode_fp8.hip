@@ -12,50 +12,66 @@
 //            "FP8/FP32 Mixed Precision")
 //   s[t]   = scale * ( q~ . c_t + q_pe . k^R_t )
 //   o~     = sum_t softmax(s)_t c_t
-// with the absorbed query q~ itself stored e4m3 with a per-row scale (so
-// q~ . c_t = qs * s_t * (q^ . c^_t)), and the chunk's partial (o~ normalised
-// by its own softmax sum, its natural-log log-sum-exp) for the combine pass.
+// with the absorbed query q~ itself stored e4m3 with one power-of-two scale
+// 2^Eq per row (q~ . c_t = 2^Eq s_t (q^ . c^_t)), and the chunk's partial (o~
+// normalised by its own softmax sum, its natural-log log-sum-exp) for the
+// combine pass.
 //
-// Mapping onto CDNA4 (4 waves, one per SIMD, 512 registers each; the same
-// plan as the bf16 kernel):
+// Mapping onto CDNA4 (4 waves, one per SIMD, 512 registers each):
 //   * Wave w owns rows 32w .. 32w+31: its e4m3 query [32 x 512] (64 VGPRs),
 //     bf16 q_pe [32 x 64] (16 VGPRs) and its output accumulator [32 x 512]
 //     f32 (the 256 accumulation registers).
-//   * Latent scores: v_mfma_scale_f32_32x32x64_f8f6f4 with unit block scales
-//     (e4m3 x e4m3; twice the bf16 rate), A = 32 c^ rows x 64 bytes from LDS
-//     (two ds_read_b128 per lane), B = the query.  Rotary scores on
-//     v_mfma_f32_32x32x16_bf16 into their own accumulator; the two meet in
-//     fp32 with the token and row scales.  Each lane ends with head l & 31
-//     and tokens 8(i >> 2) + 4(l >> 5) + (i & 3).
-//   * O^T += C^T P'^T on v_mfma_f32_32x32x16_fp8_fp8: A = c^ columns, one
-//     ds_read_b64_tr_b8 (the 8-bit LDS transpose read) per lane and MFMA,
-//     rows taken in the order the score accumulator holds the tokens; B = P'
-//     in e4m3 straight from the score registers.
-//   * P' = 2^(s - m + 8) * s_t / s_ref: e4m3 with the row maximum at 256 and
-//     the token scale folded in relative to s_ref, the largest token scale of
-//     the chunk; O accumulates in units of s_ref / 256.  m is a fixed row
-//     reference set by the row's first visible scores and never moved, so O
-//     is never rescaled.  A later score past m + 0.75 (where P' would leave
-//     e4m3's range) sends the whole workgroup through a second pass with the
-//     row's true maximum as m.  The sum l adds the e4m3-rounded P' back at
-//     s_ref / (256 s_t), so numerator and denominator carry the same
-//     rounding.
-//   * Iteration i copies tile i + 5 and runs the output product of tile
-//     i - 1 beside the scores of tile i (independent accumulators), then the
-//     softmax of tile i.  A ring of 7 stages [c^ ; k^R ; s] (20.1 KiB each)
-//     keeps five tiles in flight; each wave copies two latent rows per
-//     instruction (4), eight rotary rows (1) and eight scales (1) per tile.
+//   * Scores of a tile, in log2 units relative to a per-row reference m:
+//       v_t = g_t (2^Eq q^ . c^_t) + [ (scale log2e q_pe) . k^R_t
+//                                      + log2 s_t - m ]
+//     The latent product is v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3 x e4m3)
+//     with the row's 2^Eq as the B block scale; g_t = scale log2e s_t.  The
+//     bracket is one accumulator: a 32x32x16 bf16 "bias" MFMA whose A row of
+//     token t is (hi(log2 s_t), lo(log2 s_t), 1) and whose B column of a row
+//     is (1, 1, -m) (m rounded to bf16; hi + lo carry log2 s_t to ~2^-16),
+//     then the four rotary MFMAs on top.  So 2^v_t = s_t 2^(s[t] - m): the
+//     token's scale is already inside.  Each lane ends with head l & 31 and
+//     tokens 8(i >> 2) + 4(l >> 5) + (i & 3).
+//   * Block-scaled probabilities: per row and tile, e = ceil(max_t v_t - 8.75)
+//     and P'_t = e4m3(2^v_t / 2^e), so the tile's largest P' lies in
+//     (2^7.75, 2^8.75], below e4m3's 448, and no value needs a running
+//     rescale: 2^e is the output product's E8M0 block scale, exact.  The sum
+//     l adds the e4m3-rounded P'_t 2^e / s_t, so numerator and denominator
+//     carry the same rounding.  m is the row's maximum over the chunk's first
+//     tile and never moves; only a tile exponent past 100 (scores more than
+//     ~100 log2 units above the first tile's, where the f32 accumulator could
+//     overflow) sends the workgroup through a second pass with the row's true
+//     maximum as m.
+//   * O^T += C^T P'^T on v_mfma_scale_f32_32x32x64_f8f6f4 over a pair of
+//     tiles (64 tokens: k-block 0 = tile 2p, k-block 1 = tile 2p + 1, each
+//     with its own E8M0 scale per row).  In each lane, operand bytes 0-15 lie
+//     in k-block 0 and bytes 16-31 in k-block 1 (measured), and the block
+//     scale of k-block kb for row n comes from lane n + 32 kb.  So the B
+//     operand is the lane's own 16 probabilities of tile 2p, then its 16 of
+//     tile 2p + 1, straight from the softmax registers, and the A operand (c^
+//     columns) is four ds_read_b64_tr_b8 per lane and MFMA, two from each
+//     tile's stage, in the same token order.
+//   * Tile i's scores run beside the softmax of tile i - 1 (independent
+//     registers, so its VALU work issues while the MFMAs run); after every
+//     second tile the output product of the completed pair follows.  A ring
+//     of 7 stages [c^ ; k^R ; s] (21 KiB each) keeps four tiles in flight;
+//     each wave copies two latent rows per instruction (4), eight rotary
+//     rows (1) and eight scales (1) per tile.  Each wave keeps its own table
+//     of per-token factors (g_t, 1/s_t and the bias row), rebuilt per tile.
+//   * Keys past the sequence (or chunk) end get the bias -3e38 (so P' = 0)
+//     and the factor 1/s_t = 0; rows whose causal limit cuts a tile take a
+//     masked path for that tile only.
 //   * LDS rows are XOR-swizzled on 16-byte chunks for gfx950's LDS (64 banks
-//     of 4 bytes; a 16-byte read serves its lanes in four 16-lane cycles,
-//     lanes taken in quads, the cycle of lane l being (l >> 5, parity of
-//     bits 2..4 of l); an 8-byte transpose read serves lanes 0-31, then
-//     32-63).  Latent chunk c of token t sits at slot (c & 15) ^ key(t) of its
-//     256-byte group, key(t) = 4(t & 3) + ((t >> 2) & 3):
+//     of 4 bytes; a 16-byte read serves its lanes in four 16-lane cycles; an
+//     8-byte transpose read serves lanes 0-31, then 32-63).  Latent chunk c of
+//     token t sits at slot (c & 15) ^ key(t) of its 256-byte group, key(t) =
+//     4(t & 3) + ((t >> 2) & 3):
 //       - scores: a cycle's 16 lanes read one chunk of 16 tokens 4a + r
 //         whose a share a parity; (r, a & 3) takes each of its 16 values once;
-//       - transpose: a half-wave reads 2 adjacent chunks of 8 tokens
-//         16kb + 4hh + r and 16kb + 8 + 4hh + r (r < 4), whose keys
-//         4r + hh and 4r + hh + 2 fill the 16 slots with the chunk bit.
+//       - transpose: a half-wave reads 2 adjacent chunks of the 8 tokens
+//         b + {0, 1, 2, 3, 8, 9, 10, 11} (b = 4hh or 16 + 4hh), whose keys
+//         share bit 0 and take the other 8 values, so that the chunk bit
+//         completes the 16 slots.
 //     Rotary chunk c (0..7) of token t sits at c ^ rope_key(t), rope_key(t)
 //     = ((t >> 2) & 3) + 4((t >> 1) & 1), as in the bf16 kernel.
 #include "mla_common.hpp"
@@ -70,30 +86,53 @@ constexpr int LAT_ROW = D_LAT;                // bytes per cached e4m3 latent ro
 constexpr int ROPE_ROW = D_ROPE * 2;          // bytes per cached bf16 rotary row
 constexpr int KS_LAT = D_LAT / 64;            // fp8 score k-steps (K = 64)
 constexpr int KS_ROPE = D_ROPE / 16;          // bf16 score k-steps (K = 16)
-constexpr int KS = KS_LAT + KS_ROPE;          // 12
+constexpr int NQK = KS_LAT + 1 + KS_ROPE;     // score MFMAs per tile (13)
 constexpr int DB = D_LAT / 32;                // 32-dim output blocks
-constexpr int PV_STEPS = 2 * DB;              // two 16-token k-steps per tile
 constexpr int ROPE_OFF = kTile * LAT_ROW;     // 16 KiB
 constexpr int SCALE_OFF = ROPE_OFF + kTile * ROPE_ROW;  // 20 KiB
 constexpr int STAGE = 21 * 1024;
 constexpr int NSTAGE = 7;
-constexpr int AHEAD = NSTAGE - 2;             // tiles in flight (5)
+constexpr int AHEAD = NSTAGE - 3;             // tiles in flight (4)
 constexpr int NW = kRowsPerWG / 32;           // 4 waves
 constexpr int kThreads = 64 * NW;
 constexpr int kDma = 6;                       // copies per wave and tile
-constexpr float kShift = 8.0f;                // the row maximum maps to P' = 256
-constexpr float kSlack = 0.75f;               // P' <= 2^8.75 < 448 between rescales
+constexpr float kTop = 8.75f;                 // a tile's largest P' <= 2^8.75 < 448
+constexpr int kEmax = 100;                    // tile exponents past this are redone
+constexpr float kMasked = -3.0e38f;           // the bias of a key past the end
+constexpr uint32_t kOneBf16 = 0x3f80u;
+
+// per-token factors of one tile: g_t = scale log2e s_t, 1/s_t, and the bias
+// MFMA's A row (hi(log2 s_t), lo(log2 s_t), 1, 0, ..) as bf16
+struct Tab {
+  float g[kTile];
+  float fb[kTile];
+  uint32_t bias[kTile][4];
+};
 
 __shared__ __attribute__((aligned(1024))) uint8_t s_ring[NSTAGE * STAGE];
+__shared__ __attribute__((aligned(16))) Tab s_tab[NW][2];
 __shared__ int s_flag[NW];
-// per wave and tile, the per-token factors of the softmax: s_t / s_ref and
-// s_ref / (256 s_t) (0 past the sequence end)
-__shared__ __attribute__((aligned(16))) float s_tok[NW][2][kTile];
-static_assert(SCALE_OFF + kTile * 4 <= STAGE, "stage layout");
+static_assert(SCALE_OFF + 2 * kTile * 4 <= STAGE, "stage layout");
 
 typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(8))) uint32_t u32x8;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(2))) short i16x2;
+typedef MLA_LDS Tab LTab;
+
+// 4-byte global -> LDS copy from a wave-uniform base plus a per-lane byte
+// offset: lane l's 4 bytes land at lds_base + 4 l (see dma16_s)
+__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff,
+                                       const MLA_LDS uint8_t* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  const uint64_t b = (uint64_t)(uintptr_t)sbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"((const void*)(uintptr_t)bu)
+               : "memory", "m0");
+}
 
 __device__ __forceinline__ int lat_key(int t) { return ((t & 3) << 2) | ((t >> 2) & 3); }
 __device__ __forceinline__ int rope_key(int t) { return ((t >> 2) & 3) | (((t >> 1) & 1) << 2); }
@@ -102,31 +141,56 @@ __device__ __forceinline__ MLA_LDS uint8_t* stage_base(int st) {
   return (MLA_LDS uint8_t*)s_ring + st * STAGE;
 }
 
-__device__ __forceinline__ f32x16 mfma_lat(i32x8 a, i32x8 b, f32x16 c) {
-  // e4m3 x e4m3, unit block scales (E8M0 127 = 2^0)
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// The score MFMAs, written as volatile asm so that each stays in the step it
+// is issued in (as pure builtins the compiler sinks them toward their use in
+// the next tile's softmax, which keeps all their LDS operands alive across
+// the output product).  Consecutive MFMAs of one chain accumulate in place;
+// a VALU read of a chain's result must follow mfma_drain() unless a barrier
+// lies between them.
+//   latent: e4m3 x e4m3, A unscaled (E8M0 127 = 2^0), B (the query) scaled by
+//   the row's 2^Eq
+__device__ __forceinline__ void mfma_lat_first(f32x16& d, const i32x8& a, const i32x8& b,
+                                               int qsc) {
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %4 op_sel_hi:[0,0,0]"
+               : "=&v"(d)
+               : "v"(a), "v"(b), "v"(127), "v"(qsc));
+}
+__device__ __forceinline__ void mfma_lat(f32x16& d, const i32x8& a, const i32x8& b, int qsc) {
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+v"(d)
+               : "v"(a), "v"(b), "v"(127), "v"(qsc));
+}
+//   bias and rotary: bf16
+__device__ __forceinline__ void mfma_bf16_first(f32x16& d, const u16x8& a, const u16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_bf16(f32x16& d, const u16x8& a, const u16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
 }
 
-__device__ __forceinline__ f32x16 mfma_rope(u16x8 a, u16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+// keeps x computed at this point of the program (an empty volatile asm that
+// reads it)
+template <typename T>
+__device__ __forceinline__ void pin(const T& x) {
+  asm volatile("" ::"v"(x));
 }
 
-// acc += A B (e4m3 x e4m3) with the accumulator pinned to the accumulation
-// registers, which hold exactly the wave's output; each block is updated by
-// MFMAs only, at least 15 MFMAs apart, and mfma_drain() covers the MFMA
-// latency before anything else reads or writes the accumulators.
-__device__ __forceinline__ void mfma_pv(f32x16& acc, long a, long b) {
-  asm("v_mfma_f32_32x32x16_fp8_fp8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+// acc += A B with e4m3 operands, B scaled by 2^(sb - 127) per 32-token block,
+// the accumulator pinned to the accumulation registers, which hold exactly
+// the wave's output; each block is updated by MFMAs only, and mfma_drain()
+// covers the MFMA latency before anything else reads or writes them.
+__device__ __forceinline__ void mfma_pv(f32x16& acc, const i32x8& a, const i32x8& b, int sb) {
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+               : "+a"(acc)
+               : "v"(a), "v"(b), "v"(127), "v"(sb));
 }
 
 __device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
 
 // The copies of one tile: wave w's latent rows 8w .. 8w+7 (parts 0..3, two
-// 512-byte rows each), their rotary rows (part 4) and their scales (part 5,
-// two lanes).  Latent and rotary rows past the sequence end re-read its last
-// token; the scales of such tokens are whatever the page holds and are never
-// used unmasked.
+// 512-byte rows each), their rotary rows (part 4) and all 32 scales (part 5).  Latent and rotary rows past the sequence end re-read its last
+// token (so the output product never meets stale bytes); the scales of such
+// tokens are whatever the page holds and are never used.
 struct TileCopy {
   const uint8_t* lat;
   const uint8_t* rope;
@@ -162,7 +226,10 @@ __device__ __forceinline__ void issue_part(const TileCopy& c, int j, int w, int 
     const uint32_t off = (uint32_t)(tc * ROPE_ROW + (((lane & 7) ^ rope_key(t)) << 4));
     dma16_s(c.rope, off, dst + ROPE_OFF + w * 8 * ROPE_ROW);
   } else {
-    if (lane < 2) dma16_s(c.scale + w * 8, (uint32_t)(lane << 4), dst + SCALE_OFF + w * 32);
+    // every wave copies the tile's 32 scales (identical bytes to the same
+    // place; lanes 32-63 fill the 128 spare bytes after them), so that no
+    // lane is masked off
+    dma4_s(c.scale, (uint32_t)((lane & 31) << 2), dst + SCALE_OFF);
   }
 }
 
@@ -183,22 +250,22 @@ __device__ __forceinline__ void barrier() {
 
 struct State {
   i32x8 q8[KS_LAT];     // e4m3 query, 32 bytes per k-step (B operand)
-  u16x8 qpe[KS_ROPE];   // bf16 rotary query (B operand)
+  u16x8 qpe[KS_ROPE];   // bf16 rotary query times scale log2e (B operand)
+  u16x8 qb;             // the bias MFMA's B column: (1, 1, -m) on lanes 0-31
   f32x16 o[DB];         // O^T accumulator: lane holds head l & 31, 16 of the
                         // block's 32 latent dims
-  float qs;             // the row's query scale times the softmax scale (log2)
-                        // times s_ref
-  int len;              // the sequence length
-  float m, l;           // reference max (log2 units, scaled) and per-lane sum
+  int qsc;              // E8M0 code of the row's query scale
   int lim;              // keys visible to the lane's row: t < lim
-  float tmax;           // largest score this lane has seen (log2 units, scaled)
-  bool redo;            // a score passed m + kSlack
+  float m;              // reference (log2 units, bf16-representable)
+  float l;              // per-lane sum
+  float tmax;           // largest tile maximum seen (log2 units, absolute)
+  bool redo;            // a tile exponent passed kEmax
 };
 
 // Per-lane LDS byte offsets from a stage's base:
 //   latent scores, k-step ks, half e:  (qk ^ (((4ks & 15) ^ e) << 4)) + 256 (ks >> 2)
 //   rotary scores, k-step k:           rp ^ (2k << 4)
-//   transpose, block db, k-step kb:    (pv ^ ((2 (db & 7)) << 4)) + 256 (db >> 3) + 8192 kb
+//   transpose, block db, tokens +16j:  (pv ^ (2 (db & 7) << 4)) + 256 (db >> 3) + 8192 j
 // (the XORed bits never carry).
 struct LaneOff {
   uint32_t qk, rp, pv;
@@ -213,22 +280,19 @@ __device__ __forceinline__ LaneOff lane_offsets(int lane) {
   o.rp = (uint32_t)(ROPE_OFF + lc * ROPE_ROW + ((hh ^ rope_key(lc)) << 4));
   // transpose: lane n of its 16-lane group addresses row r = n >> 1 of the
   // read, token 4hh + r (r < 4) or 8 + 4hh + r - 4, bytes 8 (n & 1) of chunk
-  // 2db + dh
+  // 2db + dh; the second read of a tile takes the tokens 16 further on (same
+  // keys)
   const int r = n >> 1;
   const int tok = (r < 4) ? 4 * hh + r : 8 + 4 * hh + (r - 4);
   o.pv = (uint32_t)(tok * LAT_ROW + ((dh ^ lat_key(tok)) << 4) + 8 * (n & 1));
   return o;
 }
 
-// The reads take the lane's absolute LDS address for a stage (stage base +
-// lane offset): stage bases are multiples of 1 KiB, so the XORed bits 4..7
-// commute with the add, which then happens once per stage and tile instead of
-// once per read.
 __device__ __forceinline__ const MLA_LDS uint8_t* lds_at(uint32_t a) {
   return (const MLA_LDS uint8_t*)(uintptr_t)a;
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const MLA_LDS uint8_t* p) {
+__device__ __forceinline__ uint32_t lds_addr(const MLA_LDS void* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
@@ -243,232 +307,314 @@ __device__ __forceinline__ u16x8 load_r(uint32_t br, int k) {
   return *(const MLA_LDS u16x8*)lds_at(br ^ (uint32_t)((2 * k) << 4));
 }
 
-// output step j: k-step kb = j >> 4 (tokens 16kb ..), block db = j & 15
-__device__ __forceinline__ long load_v(uint32_t bv, int j) {
-  const int kb = j >> 4, db = j & 15;
-  const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-      (MLA_LDS i32x2*)(lds_at(bv ^ (uint32_t)((2 * (db & 7)) << 4)) + (db >> 3) * 256 +
-                       kb * 16 * LAT_ROW));
-  return __builtin_bit_cast(long, v);
+__device__ __forceinline__ i32x2 tr8(const MLA_LDS uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((MLA_LDS i32x2*)p);
 }
 
-constexpr int AH = 2;   // LDS reads run this many steps ahead of their MFMAs
+// the A operand of output block db: its 32 dims x the lane's 16 tokens of
+// tile 2p (stage address ba) then the same 16 of tile 2p + 1 (bb), in the
+// order of the probability bytes: 4hh + 0..3, 8 + 4hh + 0..3, then 16 further
+__device__ __forceinline__ i32x8 load_v(uint32_t ba, uint32_t bb, int db) {
+  const uint32_t x = (uint32_t)((2 * (db & 7)) << 4);
+  const int o = (db >> 3) * 256;
+  const MLA_LDS uint8_t* pa = lds_at(ba ^ x) + o;
+  const MLA_LDS uint8_t* pb = lds_at(bb ^ x) + o;
+  const i32x2 a = tr8(pa), b = tr8(pa + 16 * LAT_ROW), c = tr8(pb), d = tr8(pb + 16 * LAT_ROW);
+  return i32x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
-// One pipeline step group: the scores of tile stage st_qk (if QK: 8 latent
-// and 4 rotary MFMAs) and the output product of stage st_pv with the e4m3
-// probabilities p (if PV: 32 MFMAs), issued alternately while both run, plus
-// the copies of a later tile (cp), issued at the start of steps 0, 2, .. 10.
-template <bool QK, bool PV, bool COPY>
-__device__ __forceinline__ void tile_step(State& S, int st_qk, int st_pv, long p0, long p1,
-                                          int lane, LaneOff lo, const TileCopy& cp, int w,
-                                          float sr0, f32x16& sl, f32x16& sr) {
-  constexpr int NSTEP = PV ? PV_STEPS : KS;
-  static_assert(2 * (kDma - 1) < KS, "the copies fit in the score steps");
-  const uint32_t bq = lds_addr(stage_base(st_qk)) + lo.qk;
-  const uint32_t br = lds_addr(stage_base(st_qk)) + lo.rp;
-  const uint32_t bv = lds_addr(stage_base(st_pv)) + lo.pv;
-  i32x8 ka[AH];
-  u16x8 ra[AH];
-  long va[AH];
-  if (QK) {
-    sl = f32x16{};
-    sr = f32x16{} + sr0;
-  }
+// The per-token table of the tile in stage st, for this wave: lane l forms
+// token (l & 31)'s entry.  Tokens at or past `end` are keys past the sequence or chunk end.
+__device__ __forceinline__ void build_table(const DecodeArgs& a, int st, int tok0, int end,
+                                            LTab* tab, int lane) {
+  const int t = lane & 31;
+  const float s = *(const MLA_LDS float*)(stage_base(st) + SCALE_OFF + 4 * t);
+  const bool in = tok0 + t < end;
+  // (scales of visible tokens are normal positive numbers, a precondition of
+  // the call)
+  const float h = in ? __log2f(s) : kMasked;
+  const uint32_t hb = pack_bf16x2(h, 0.f) & 0xffffu;
+  const float hl = in ? h - __uint_as_float(hb << 16) : 0.f;
+  const uint32_t w0 = hb | (pack_bf16x2(hl, 0.f) << 16);
+  // (both half-waves write the same values to the same places)
+  tab->g[t] = in ? s * a.scale_log2 : 0.f;
+  tab->fb[t] = in ? __builtin_amdgcn_rcpf(s) : 0.f;
+  *(MLA_LDS u32x4*)tab->bias[t] = u32x4{w0, kOneBf16, 0u, 0u};
+}
+
+// The softmax of one tile, cut into slices that a score step runs between its
+// MFMAs.  Inputs: the tile's score accumulators (sl, sr), its table and first
+// token.  Outputs: the e4m3 probabilities pk (tokens 8g + 4hh + 0..3 in byte
+// order, g = 0..3) and the E8M0 code of the row's block scale; l and the row
+// state are updated in place.
+struct Softmax {
+  f32x16 sl, sr;
+  const LTab* tab;
+  f32x4 gv[4], fv[4];
+  float v[16];
+  float mx;
+  float sc;         // 2^e
+  int code;
+  uint32_t pk[4];
+
+  // first: the chunk's first tile in a pass that sets the reference m from it
+  template <int J>
+  __device__ __forceinline__ void slice(State& S, int lane, bool first = false) {
+    const int hh = lane >> 5;
+    if constexpr (J == 0) {
 #pragma unroll
-  for (int j = 0; j < AH; ++j) {
-    if (QK) ka[j] = load_k(bq, j);
-    if (PV) va[j] = load_v(bv, j);
-  }
+      for (int g = 0; g < 4; ++g) gv[g] = *(const MLA_LDS f32x4*)&tab->g[8 * g + 4 * hh];
+    } else if constexpr (J >= 1 && J <= 4) {
+      constexpr int g = J - 1;
 #pragma unroll
-  for (int j = 0; j < NSTEP; ++j) {
-    // a copy is issued while the previous step's MFMA still runs
-    if (COPY && j % 2 == 0 && j / 2 < kDma) issue_part(cp, j / 2, w, lane);
-    if (QK && j < KS_LAT) {
-      const i32x8 cur = ka[j % AH];
-      if (j + AH < KS_LAT) ka[j % AH] = load_k(bq, j + AH);
-      else ra[(j + AH - KS_LAT) % AH] = load_r(br, j + AH - KS_LAT);
-      sl = mfma_lat(cur, S.q8[j], sl);
-    } else if (QK && j < KS) {
-      const int k = j - KS_LAT;
-      const u16x8 cur = ra[k % AH];
-      if (k + AH < KS_ROPE) ra[k % AH] = load_r(br, k + AH);
-      sr = mfma_rope(cur, S.qpe[k], sr);
+      for (int r = 0; r < 4; ++r) {
+        v[4 * g + r] = fmaf(sl[4 * g + r], gv[g][r], sr[4 * g + r]);
+        pin(v[4 * g + r]);
+      }
+    } else if constexpr (J == 5) {
+      const float m0 = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+      const float m1 = fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7]));
+      const float m2 = fmaxf(fmaxf(v[8], v[9]), fmaxf(v[10], v[11]));
+      const float m3 = fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15]));
+      mx = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+      pin(mx);
+    } else if constexpr (J == 6) {
+      // the row's tile maximum: the other half-wave holds the row's other 16
+      // tokens
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                       false, false);
+      mx = fmaxf(mx, __uint_as_float(hh ? sw[0] : sw[1]));
+      if (first) {
+        // the reference: the first tile's maximum rounded to bf16 (0 for a
+        // row that sees none of its keys)
+        const float mr = mx > 0.5f * kMasked
+                             ? __uint_as_float((pack_bf16x2(mx, 0.f) & 0xffffu) << 16)
+                             : 0.f;
+        S.m = mr;
+        S.tmax = mx;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] -= mr;
+        mx -= mr;
+      } else {
+        S.tmax = fmaxf(S.tmax, mx + S.m);
+      }
+      const float ef = fminf(fmaxf(__builtin_ceilf(mx - kTop), -126.f), 200.f);
+      S.redo |= ef > (float)kEmax;
+      const int e = min((int)ef, 127);
+      code = e + 127;
+      sc = __uint_as_float((uint32_t)code << 23);
+      pin(code);
+      pin(sc);
+    } else if constexpr (J >= 7 && J <= 10) {
+      constexpr int g = J - 7;
+      float x[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[r] = fast_exp2(v[4 * g + r]);
+      const i16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(i16x2{0, 0}, x[0], x[1], sc, false);
+      const i16x2 w = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x[2], x[3], sc, true);
+      pk[g] = __builtin_bit_cast(uint32_t, w);
+      pin(pk[g]);
+    } else if constexpr (J == 11) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) fv[g] = *(const MLA_LDS f32x4*)&tab->fb[8 * g + 4 * hh];
+    } else if constexpr (J == 12 || J == 13) {
+      // l += P' 2^e / s_t over the lane's tokens (the scaled conversion gives
+      // P' 2^e exactly)
+      float acc = 0.f;
+#pragma unroll
+      for (int g = 2 * (J - 12); g < 2 * (J - 12) + 2; ++g) {
+        const f32x2 b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pk[g], sc, false);
+        const f32x2 b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pk[g], sc, true);
+        acc = fmaf(b01[0], fv[g][0], acc);
+        acc = fmaf(b01[1], fv[g][1], acc);
+        acc = fmaf(b23[0], fv[g][2], acc);
+        acc = fmaf(b23[1], fv[g][3], acc);
+      }
+      S.l += acc;
+      pin(S.l);
     }
-    if (PV) {
-      const long cur = va[j % AH];
-      if (j + AH < PV_STEPS) va[j % AH] = load_v(bv, j + AH);
-      mfma_pv(S.o[j & (DB - 1)], cur, (j >> 4) ? p1 : p0);
+  }
+
+  __device__ __forceinline__ void all(State& S, int lane, bool first) {
+    slice<0>(S, lane);
+    slice<1>(S, lane);
+    slice<2>(S, lane);
+    slice<3>(S, lane);
+    slice<4>(S, lane);
+    slice<5>(S, lane);
+    slice<6>(S, lane, first);
+    slice<7>(S, lane);
+    slice<8>(S, lane);
+    slice<9>(S, lane);
+    slice<10>(S, lane);
+    slice<11>(S, lane);
+    slice<12>(S, lane);
+    slice<13>(S, lane);
+  }
+};
+
+// Rows whose causal limit falls in the tile (starting at tok0): their keys at
+// or past the limit get the score kMasked through the bias accumulator (a
+// uniform branch, taken on such tiles only).
+__device__ __forceinline__ void mask_rows(const State& S, f32x16& sr, int tok0, int lane) {
+  if (__ballot(tok0 + kTile > S.lim) != 0) {
+    mfma_drain();
+    // keys t = tok0 + 4hh + 8(i >> 2) + (i & 3)
+    const int r = S.lim - tok0 - 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (8 * (i >> 2) + (i & 3) >= r) sr[i] = kMasked;
+  }
+}
+
+// The scores of the tile in stage st into (sl, sr): 8 latent MFMAs, the bias
+// MFMA and 4 rotary MFMAs, with (SM) the softmax of the previous tile run in
+// slices between them and (COPY) the copies of a later tile issued at steps
+// 0, 2, .. 10.  Operand reads run two steps ahead of their MFMAs.
+template <bool SM, bool COPY>
+__device__ __forceinline__ void score_step(State& S, int st, const LTab* tab, f32x16& sl,
+                                           f32x16& sr, Softmax& prev, int lane, LaneOff lo,
+                                           const TileCopy& cp, int w) {
+  const uint32_t bq = lds_addr(stage_base(st)) + lo.qk;
+  const uint32_t br = lds_addr(stage_base(st)) + lo.rp;
+  i32x8 ka0 = load_k(bq, 0), ka1 = load_k(bq, 1);
+  u16x8 ra0, ra1, bias;
+#pragma unroll
+  for (int j = 0; j < NQK; ++j) {
+    if (COPY && j % 2 == 0 && j / 2 < kDma) issue_part(cp, j / 2, w, lane);
+    if (j < KS_LAT) {
+      const i32x8 cur = (j & 1) ? ka1 : ka0;
+      if (j + 2 < KS_LAT) {
+        if (j & 1) ka1 = load_k(bq, j + 2);
+        else ka0 = load_k(bq, j + 2);
+      } else if (j + 2 == KS_LAT) {
+        bias = *(const MLA_LDS u16x8*)tab->bias[lane & 31];
+      } else {
+        ra0 = load_r(br, 0);
+      }
+      if (j == 0) mfma_lat_first(sl, cur, S.q8[j], S.qsc);
+      else mfma_lat(sl, cur, S.q8[j], S.qsc);
+    } else if (j == KS_LAT) {
+      ra1 = load_r(br, 1);
+      mfma_bf16_first(sr, bias, S.qb);
+    } else {
+      const int k = j - KS_LAT - 1;
+      const u16x8 cur = (k & 1) ? ra1 : ra0;
+      if (k + 2 < KS_ROPE) {
+        if (k & 1) ra1 = load_r(br, k + 2);
+        else ra0 = load_r(br, k + 2);
+      }
+      mfma_bf16(sr, cur, S.qpe[k]);
+    }
+    if constexpr (SM) {
+      switch (j) {
+        case 0: prev.template slice<0>(S, lane); break;
+        case 1: prev.template slice<1>(S, lane); break;
+        case 2: prev.template slice<2>(S, lane); break;
+        case 3: prev.template slice<3>(S, lane); break;
+        case 4: prev.template slice<4>(S, lane); break;
+        case 5: prev.template slice<5>(S, lane); break;
+        case 6: prev.template slice<6>(S, lane); break;
+        case 7: prev.template slice<7>(S, lane); break;
+        case 8: prev.template slice<8>(S, lane); break;
+        case 9: prev.template slice<9>(S, lane); break;
+        case 10: prev.template slice<10>(S, lane); break;
+        case 11: prev.template slice<11>(S, lane); break;
+        case 12:
+          prev.template slice<12>(S, lane);
+          prev.template slice<13>(S, lane);
+          break;
+        default: break;
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// The softmax of one tile.  Lane holds head l & 31 and tokens
-// 8(i >> 2) + 4hh + (i & 3).  On the chunk's first tile (first) a row's
-// first scores set its reference m (the row's two lanes exchange their
-// maxima); later tiles use it as it is, so the output is never rescaled, and
-// their rotary accumulator starts at shift = 8 - m, so that the scores arrive
-// already in the exponent of P'.  A score above m + kSlack (where P' would
-// leave e4m3's range) marks the workgroup for a second pass with the true row
-// maxima.  Returns the e4m3 probabilities as the two B operands (tokens
-// 16kb .. of k-step kb) and adds them to the lane's sum.
-__device__ __forceinline__ void tile_probs(const DecodeArgs& a, State& S, const f32x16& sl,
-                                           const f32x16& sr, const MLA_LDS uint8_t* base,
-                                           int tok0, int w, int lane, float inv_sref,
-                                           float sref_256, bool first, float shift0, long& p0,
-                                           long& p1) {
-  const int hh = lane >> 5;
-  // the per-token factors, once per tile and wave: lane l < 32 forms token
-  // l's, the lanes read back the 16 they need (LDS is in order per wave).
-  // (Scales of visible tokens are normal positive numbers, a precondition of
-  // the call; a zero one would make fb infinite.)
-  {
-    const int t = lane & 31;
-    const float st = *(const MLA_LDS float*)(base + SCALE_OFF + 4 * t);
-    const bool in = tok0 + t < S.len;
-    const float fa = in ? st * inv_sref : 0.f;
-    const float fb = in ? sref_256 * __builtin_amdgcn_rcpf(st) : 0.f;
-    if (lane < 32) {
-      s_tok[w][0][t] = fa;
-      s_tok[w][1][t] = fb;
+// The output product of a pair: the lane's probabilities of tile 2p (pa,
+// block code ca) and of tile 2p + 1 (pb, cb) times the c^ columns of stages
+// sa and sb.
+__device__ __forceinline__ void pv_step(State& S, const uint32_t (&pa)[4], int ca,
+                                        const uint32_t (&pb)[4], int cb, int sa, int sb, int lane,
+                                        LaneOff lo) {
+  const i32x8 b = i32x8{(int)pa[0], (int)pa[1], (int)pa[2], (int)pa[3],
+                        (int)pb[0], (int)pb[1], (int)pb[2], (int)pb[3]};
+  // (the block scale of k-block kb comes from lanes 32 kb ..)
+  const int code = (lane >> 5) ? cb : ca;
+  const uint32_t ba = lds_addr(stage_base(sa)) + lo.pv;
+  const uint32_t bb = lds_addr(stage_base(sb)) + lo.pv;
+  i32x8 va0 = load_v(ba, bb, 0), va1 = load_v(ba, bb, 1);
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    const i32x8 cur = (db & 1) ? va1 : va0;
+    if (db + 2 < DB) {
+      if (db & 1) va1 = load_v(ba, bb, db + 2);
+      else va0 = load_v(ba, bb, db + 2);
     }
+    mfma_pv(S.o[db], cur, b, code);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  // the factors of the lane's tokens: 4 groups of 4 consecutive tokens
-  f32x4 fa[4], fb[4];
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    fa[g] = *(const MLA_LDS f32x4*)&s_tok[w][0][8 * g + 4 * hh];
-    fb[g] = *(const MLA_LDS f32x4*)&s_tok[w][1][8 * g + 4 * hh];
-  }
-  // scores in log2 units: the latent part is sl * s_t * qs = sl * fa * (qs
-  // s_ref), and the rotary query and qs carry the softmax scale
-  float sv[16];
-  float mx = -INFINITY;
-  const bool cut = __ballot(tok0 + kTile > S.lim) != 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float v = fmaf(sl[i], fa[i >> 2][i & 3] * S.qs, sr[i]);
-    if (cut && tok0 + 8 * (i >> 2) + 4 * hh + (i & 3) >= S.lim) v = -INFINITY;
-    sv[i] = v;
-    mx = fmaxf(mx, v);
-  }
-  float shift;
-  if (first) {
-    S.tmax = fmaxf(S.tmax, mx);
-    if (__ballot(mx > S.m + kSlack)) {
-      const float rmx = wave_max_xor(mx, 32);
-      const float mass = wave_sum_xor(S.l, 32);
-      if (rmx > S.m + kSlack && mass == 0.f) S.m = rmx;
-    }
-    S.redo |= mx > S.m + kSlack;
-    // (a row without reference has no visible key: P' = 0)
-    shift = kShift - (S.m == -INFINITY ? INFINITY : S.m);
-  } else {
-    // the scores carry shift0 already; (-inf - -inf = NaN for a row without
-    // reference, which fmaxf ignores)
-    S.tmax = fmaxf(S.tmax, mx - shift0);
-    S.redo |= mx > kShift + kSlack;
-    shift = 0.f;
-  }
-  // P' = 2^(s - m + 8) * s_t / s_ref in e4m3, and l += P' * s_ref / (256 s_t)
-  uint32_t pk[4];
-  float lsum = 0.f;
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {
-    float x[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) x[r] = fast_exp2(sv[4 * g + r] + shift) * fa[g][r];
-    // (saturating: a probability past 448 only occurs in a pass that is redone)
-    int pw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
-    pw = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pw, true);
-    pk[g] = (uint32_t)pw;
-    const f32x2 b01 = __builtin_amdgcn_cvt_pk_f32_fp8(pw, false);
-    const f32x2 b23 = __builtin_amdgcn_cvt_pk_f32_fp8(pw, true);
-    lsum = fmaf(b01[0], fb[g][0], lsum);
-    lsum = fmaf(b01[1], fb[g][1], lsum);
-    lsum = fmaf(b23[0], fb[g][2], lsum);
-    lsum = fmaf(b23[1], fb[g][3], lsum);
-  }
-  S.l += lsum;
-  p0 = (long)(((uint64_t)pk[1] << 32) | pk[0]);
-  p1 = (long)(((uint64_t)pk[3] << 32) | pk[2]);
 }
 
-// The chunk's one pass over its tiles [k0, k0 + n).
-//   * Prologue: the page window; the loads of the chunk's token scales (for
-//     s_ref, the largest of them); the copies of tiles 0 and 1; the query.
-//     All of these land before the first barrier, and the query registers
-//     are marked used there, so that no wait the compiler places for its
-//     own loads can fall behind a later copy.  Tiles 2 .. AHEAD follow.
-//   * Iteration i (1 <= i < n) waits for tile i (this wave's copies are done
-//     once at most AHEAD - 1 newer tiles' are outstanding; after the barrier
-//     every wave's are, and every wave is done with stage (i - 2) % NSTAGE),
-//     copies tile i + AHEAD into that stage, runs the output product of tile
-//     i - 1 beside the scores of tile i and then the softmax of tile i.
-//     Every iteration copies one tile (past the chunk's last tile, a re-read
-//     of it into a stage that is not read again), so each wait count is a
-//     constant.
-template <bool FIRST, typename LoadQuery>
+// The chunk's one pass over its tiles [k0, k0 + n), as pairs (a last odd
+// tile pairs with a phantom tile whose keys all lie past the chunk end).
+//   * Prologue: the page window, the copies of tiles 0 and 1 and the query,
+//     all landed before the first barrier (the query registers are marked
+//     used there, so that no wait the compiler places for its own loads can
+//     fall behind a later copy), then tiles 2 .. AHEAD.  Tile 0's scores and
+//     softmax set each row's reference m (first pass); tile 1's scores
+//     follow.
+//   * Tile i (i >= 1): wait for it (this wave's copies are done once at most
+//     AHEAD - 1 newer tiles' are outstanding; after the barrier every wave's
+//     are, and every wave is done with the pair before last, whose stages the
+//     next copies reuse), copy tile i + AHEAD, build its table, run its
+//     scores beside the softmax of tile i - 1 and, for even i, the output
+//     product of the pair that softmax completed.  Every tile copies one tile
+//     (past the chunk's last tile, a re-read of it into a stage that is not
+//     read again), so each wait count is a constant.
+template <typename LoadQuery>
 __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Chunk& ch, int k0,
-                                         int n, int w, int lane, LoadQuery load_query,
-                                         float& inv_sref, float& sref_256) {
-  static_assert(AHEAD + 2 <= NSTAGE, "ring");
+                                         int n, int w, int lane, bool first,
+                                         LoadQuery load_query) {
+  static_assert(AHEAD + 3 <= NSTAGE, "ring");
+  // (a fresh copy of the lane index, so that the per-lane constants below are
+  // formed here and not kept alive across the whole pass from the kernel's
+  // start, where they would be spilled around the loop)
+  asm volatile("" : "+v"(lane));
   const LaneOff lo = lane_offsets(lane);
   const int32_t* bt_row = a.block_table + (int64_t)ch.b * a.max_pages;
   PageWindow W;
   W.pg0 = uni(k0 * kTile / kPage);
   W.v = page_window_load(bt_row, a.max_pages, W.pg0, lane);
   const int k_last = k0 + n - 1;
-  auto copy_of = [&](int k, int st) {
-    k = min(k, k_last);
+  const int np = (n + 1) >> 1;
+  const int end = min(ch.len, (k0 + n) * kTile);   // keys at or past end are masked
+  auto copy_of = [&](int i) {
+    const int k = min(k0 + i, k_last);
     const int page = page_lookup(W, bt_row, a.max_pages, k * kTile / kPage, lane);
-    return tile_copy(a, page, ch.len, k, st);
+    return tile_copy(a, page, ch.len, k, i % NSTAGE);
   };
-  // the chunk's token scales, pages from the window: the first 1024 tokens
-  // in one batch of loads (their pages always lie in the window), the rest
-  // four loads per lane and round (a direct table read past the window)
-  const int t_begin = k0 * kTile, t_end = min((k_last + 1) * kTile, ch.len);
-  float sref = 0.f;
-  for (int t0 = t_begin + 16 * 64; FIRST && t0 < t_end; t0 += 4 * 64) {
-    float v[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = t0 + 64 * u + lane;
-      const int rel = (t >> 6) - W.pg0;
-      // (every lane takes part in the shuffle: a lane outside the window
-      // reads the table directly)
-      const int wpage = __shfl(W.v, rel & 63, 64);
-      const int page = rel < 64 ? wpage : bt_row[min(t, t_end - 1) >> 6];
-      v[u] = t < t_end ? a.kv_scale[(int64_t)page * kPage + (t & (kPage - 1))] : 0.f;
-    }
-    sref = fmaxf(sref, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
-  }
-  float v[16];
-  if (FIRST) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int t = t_begin + 64 * u + lane;
-      const int page = __shfl(W.v, ((t >> 6) - W.pg0) & 63, 64);
-      v[u] = t < t_end ? a.kv_scale[(int64_t)page * kPage + (t & (kPage - 1))] : 0.f;
-    }
-  }
-  issue_tile(copy_of(k0, 0), w, lane);
-  issue_tile(copy_of(k0 + 1, 1), w, lane);
-  if (FIRST) load_query();
+  LTab* tab0 = (LTab*)&s_tab[w][0];
+  LTab* tab1 = (LTab*)&s_tab[w][1];
+  // the bias B column: (1, 1, -m) for k = 0..2 on lanes 0-31, zero elsewhere
+  auto set_qb = [&]() {
+    const uint32_t mneg = pack_bf16x2(-S.m, 0.f) & 0xffffu;
+    S.qb = (lane >> 5) ? u16x8{}
+                       : __builtin_bit_cast(u16x8, u32x4{kOneBf16 | (kOneBf16 << 16), mneg, 0u, 0u});
+  };
+
+  issue_tile(copy_of(0), w, lane);
+  issue_tile(copy_of(1), w, lane);
+  if (first) load_query();
   wait_vm<0>();
-  if (FIRST) {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) sref = fmaxf(sref, v[u]);
-  }
-  if (FIRST) {
+  if (first) {
 #pragma unroll
     for (int kk = 0; kk < KS_LAT; ++kk) asm volatile("" ::"v"(S.q8[kk]));
 #pragma unroll
     for (int kk = 0; kk < KS_ROPE; ++kk) asm volatile("" ::"v"(S.qpe[kk]));
-    asm volatile("" ::"v"(S.qs));
+    asm volatile("" ::"v"(S.qsc));
     // the softmax scale (log2 units) goes into the rotary query (rounded to
-    // bf16 again: 2^-9 relative on the rotary part of a score) and into the
-    // row scale
+    // bf16 again: 2^-9 relative on the rotary part of a score)
 #pragma unroll
     for (int kk = 0; kk < KS_ROPE; ++kk) {
       u16x8 v = S.qpe[kk];
@@ -481,35 +627,66 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
       }
       S.qpe[kk] = v;
     }
-    S.qs *= a.scale_log2;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) sref = fmaxf(sref, __shfl_xor(sref, m, 64));
-    if (!(sref > 0.f)) sref = 1.f;
-    inv_sref = 1.0f / sref;
-    sref_256 = sref * (1.0f / 256.0f);
-    S.qs *= sref;
+    S.m = 0.f;   // until the first tile sets it
   }
+  set_qb();
+  build_table(a, 0, k0 * kTile, end, tab0, lane);
   barrier();
 #pragma unroll
-  for (int i = 2; i <= AHEAD; ++i) issue_tile(copy_of(k0 + i, i), w, lane);
+  for (int i = 2; i <= AHEAD; ++i) issue_tile(copy_of(i), w, lane);
 
-  long p0, p1;
-  f32x16 sl, sr;
-  tile_step<true, false, false>(S, 0, 0, 0, 0, lane, lo, TileCopy{}, w, 0.f, sl, sr);
-  tile_probs(a, S, sl, sr, stage_base(0), k0 * kTile, w, lane, inv_sref, sref_256, true, 0.f,
-             p0, p1);
-  const float shift = kShift - (S.m == -INFINITY ? INFINITY : S.m);
-  for (int i = 1; i < n; ++i) {
+  Softmax sa, sb;   // tiles 2p (its pk, code kept for the pair's product), 2p + 1
+  sa.tab = tab0;
+  score_step<false, false>(S, 0, tab0, sa.sl, sa.sr, sb, lane, lo, TileCopy{}, w);
+  mask_rows(S, sa.sr, k0 * kTile, lane);
+  mfma_drain();
+  sa.all(S, lane, first);
+  if (first) set_qb();
+  {
     wait_vm<(AHEAD - 1) * kDma>();
     barrier();
-    const int st = i % NSTAGE;
-    const TileCopy c = copy_of(k0 + i + AHEAD, (i + AHEAD) % NSTAGE);
-    tile_step<true, true, true>(S, st, (i - 1) % NSTAGE, p0, p1, lane, lo, c, w, shift, sl, sr);
-    tile_probs(a, S, sl, sr, stage_base(st), (k0 + i) * kTile, w, lane, inv_sref, sref_256,
-               false, shift, p0, p1);
+    const TileCopy c = copy_of(1 + AHEAD);
+    build_table(a, 1, (k0 + 1) * kTile, end, tab1, lane);
+    sb.tab = tab1;
+    score_step<false, true>(S, 1, tab1, sb.sl, sb.sr, sa, lane, lo, c, w);
+    mask_rows(S, sb.sr, (k0 + 1) * kTile, lane);
   }
-  tile_step<false, true, false>(S, 0, (n - 1) % NSTAGE, p0, p1, lane, lo, TileCopy{}, w, 0.f, sl,
-                                sr);
+  for (int p = 1; p < np; ++p) {
+    const int i0 = 2 * p;
+    // tile 2p: its scores beside the softmax of tile 2p - 1, then the output
+    // product of pair p - 1
+    {
+      wait_vm<(AHEAD - 1) * kDma>();
+      barrier();
+      const TileCopy c = copy_of(i0 + AHEAD);
+      build_table(a, i0 % NSTAGE, (k0 + i0) * kTile, end, tab0, lane);
+      f32x16 nsl, nsr;
+      score_step<true, true>(S, i0 % NSTAGE, tab0, nsl, nsr, sb, lane, lo, c, w);
+      mask_rows(S, nsr, (k0 + i0) * kTile, lane);
+      pv_step(S, sa.pk, sa.code, sb.pk, sb.code, (i0 - 2) % NSTAGE, (i0 - 1) % NSTAGE, lane, lo);
+      sa.sl = nsl;
+      sa.sr = nsr;
+      sa.tab = tab0;
+    }
+    // tile 2p + 1: its scores beside the softmax of tile 2p
+    {
+      wait_vm<(AHEAD - 1) * kDma>();
+      barrier();
+      const TileCopy c = copy_of(i0 + 1 + AHEAD);
+      build_table(a, (i0 + 1) % NSTAGE, (k0 + i0 + 1) * kTile, end, tab1, lane);
+      f32x16 nsl, nsr;
+      score_step<true, true>(S, (i0 + 1) % NSTAGE, tab1, nsl, nsr, sa, lane, lo, c, w);
+      mask_rows(S, nsr, (k0 + i0 + 1) * kTile, lane);
+      sb.sl = nsl;
+      sb.sr = nsr;
+      sb.tab = tab1;
+    }
+  }
+  // the last tile's softmax and the last pair's output product
+  mfma_drain();
+  sb.all(S, lane, false);
+  pv_step(S, sa.pk, sa.code, sb.pk, sb.code, (2 * np - 2) % NSTAGE, (2 * np - 1) % NSTAGE, lane,
+          lo);
   // (the last re-reads must land before the stages are reused or the
   // workgroup ends)
   wait_vm<0>();
@@ -521,14 +698,14 @@ constexpr int O_PITCH = D_LAT * 2 + 16;
 static_assert(NW * 32 * O_PITCH <= NSTAGE * STAGE, "the staged rows fit the ring");
 
 __device__ __forceinline__ void write_partial(const DecodeArgs& a, const State& S, int64_t slot,
-                                              float sref_256, int w, int lane) {
+                                              int w, int lane) {
   const int lc = lane & 31, hh = lane >> 5;
   mfma_drain();
   const float lsum = wave_sum_xor(S.l, 32);
   const int row = w * 32 + lc;
   if (hh == 0) a.part_lse[slot * kRowsPerWG + row] =
       lsum > 0.f ? (S.m + __log2f(lsum)) * kLn2 : -INFINITY;
-  const float f = lsum > 0.f ? sref_256 / lsum : 0.f;
+  const float f = lsum > 0.f ? 1.0f / lsum : 0.f;
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   barrier();
   MLA_LDS uint8_t* st = (MLA_LDS uint8_t*)s_ring + w * 32 * O_PITCH;
@@ -576,12 +753,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
   State S;
 #pragma unroll
   for (int db = 0; db < DB; ++db) S.o[db] = f32x16{};
-  S.m = -INFINITY;
+  S.m = 0.f;
   S.l = 0.f;
   S.lim = valid ? (a.causal ? ch.len - a.q_len + j + 1 : ch.len) : 0;
   S.tmax = -INFINITY;
   S.redo = false;
-  S.len = ch.len;
   auto load_query = [&]() {
     // (a row past the end reads row 0; its limit 0 masks every key)
     const uint8_t* q8 = (const uint8_t*)a.q_lat + qrow * D_LAT;
@@ -590,29 +766,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
     for (int kk = 0; kk < KS_LAT; ++kk) S.q8[kk] = *(const i32x8*)(q8 + kk * 64 + hh * 32);
 #pragma unroll
     for (int kk = 0; kk < KS_ROPE; ++kk) S.qpe[kk] = *(const u16x8*)(qpe + kk * 16 + hh * 8);
-    S.qs = a.q_scale[qrow];
+    // the row scale is a power of two (the absorb pass writes it so): its
+    // exponent field is the E8M0 code
+    S.qsc = (int)((__float_as_uint(a.q_scale[qrow]) >> 23) & 0xffu);
   };
 
-  float inv_sref, sref_256;
-  run_pass<true>(a, S, ch, k0, n, w, lane, load_query, inv_sref, sref_256);
-
-  // rare second pass, with the true row maxima as references, when any row
-  // of the workgroup saw a score past its reference + kSlack
-  if (lane == 0) s_flag[w] = S.redo ? 1 : 0;
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  barrier();
-  const bool any_redo = __ballot(lane < NW && s_flag[lane & (NW - 1)] != 0) != 0;
-  if (any_redo) {
-    S.m = wave_max_xor(S.tmax, 32);
+  // the pass, and a rare second one with the true row maxima as references
+  // when any tile exponent of the workgroup passed kEmax
+#pragma clang loop unroll(disable)
+  for (int pass = 0; pass < 2; ++pass) {
+    run_pass(a, S, ch, k0, n, w, lane, pass == 0, load_query);
+    if (pass == 1) break;
+    if (lane == 0) s_flag[w] = S.redo ? 1 : 0;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    barrier();
+    const bool any_redo = __ballot(lane < NW && s_flag[lane & (NW - 1)] != 0) != 0;
+    if (!any_redo) break;
+    // (rounded to bf16 like every reference; a row without visible keys
+    // keeps m = 0)
+    if (S.tmax > 0.5f * kMasked)
+      S.m = __uint_as_float((pack_bf16x2(S.tmax, 0.f) & 0xffffu) << 16);
     S.l = 0.f;
     mfma_drain();
 #pragma unroll
     for (int db = 0; db < DB; ++db) S.o[db] = f32x16{};
-    // (the pass's first copies go into stages 0 and 1: the barrier above
-    // follows every wave's last read of them)
-    run_pass<false>(a, S, ch, k0, n, w, lane, [] {}, inv_sref, sref_256);
+    // (the second pass's first copies go into stages 0 and 1: the barrier
+    // above follows every wave's last read of them)
   }
-  write_partial(a, S, slot, sref_256, w, lane);
+  write_partial(a, S, slot, w, lane);
 }
 
 }  // namespace

@@ -117,7 +117,9 @@ typedef struct {
  *            act dtype for BF16/F32 latents; for FP8_E4M3 latents, e4m3 codes
  *            of q~ / q_latent_scale
  *   q_latent_scale out [batch, q_len, n_heads] f32 (FP8_E4M3 latent only,
- *            = max|q~| / 448 per row; must be NULL otherwise)
+ *            one power of two per row: the smallest 2^k with
+ *            max|q~| / 2^k <= 448, 1 for an all-zero row; must be NULL
+ *            otherwise)
  *   q_pe     out [batch, q_len, n_heads, d_rope] act dtype: q^R with adjacent
  *            pairs (x_2i, x_2i+1) rotated by pos * rope_base^(-2i/d_rope); the
  *            angle is formed in fp64, the rotation is done in fp32

@@ -21,13 +21,15 @@ E4M3_MAX = 448.0
 def quantize_rows_e4m3(x):
     """Each row of x as OCP e4m3 codes times one per-row scale, decoded back.
 
-    The scale is max|row| / 448, so the row's largest magnitude maps to the
-    largest finite e4m3 value (1 for an all-zero row); codes are rounded to
-    nearest-even by the oracle's codec.
+    The scale is the smallest power of two 2^k with max|row| / 2^k <= 448, so
+    the row's largest magnitude lands in (224, 448] (1 for an all-zero row);
+    codes are rounded to nearest-even by the oracle's codec.
     """
     x = np.asarray(x, dtype=np.float64)
     amax = np.max(np.abs(x), axis=-1, keepdims=True)
-    scale = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    mant, ex = np.frexp(np.where(amax > 0, amax / E4M3_MAX, 1.0))
+    ex = np.where(mant == 0.5, ex - 1, ex)
+    scale = np.where(amax > 0, np.ldexp(1.0, np.clip(ex, -126, 127)), 1.0)
     return oracle.e4m3_bits_to_f64(oracle.f64_to_e4m3_bits(x / scale)) * scale
 
 

@@ -180,18 +180,22 @@ def test_score_jumps_force_second_pass():
     check_against_oracle(wl, got, rows=sample_rows(wl, 10, seed=4))
 
 
-def test_score_jumps_force_second_pass_fp8_cache():
-    """The e4m3-cache kernel's second pass, taken when a score passes its
-    row's reference by more than 0.75 (log2 units), is right.
+@pytest.mark.parametrize("late", [(28, 31), (60, 63)], ids=["one_pass", "second_pass"])
+def test_score_jumps_fp8_cache(late):
+    """Scores that jump far above the first tile's inside a chunk are right on
+    the e4m3-cache kernel.
 
-    As in the bf16 case the absorbed query is exactly 64 * e_0, whose e4m3
-    code is 448 with row scale 64 / 448.  Latent dim 0 of token t holds k_t:
-    code 448 with token scale k_t / 448 where k_t > 0, code 0 (scale as
-    generated) where k_t = 0; the other dims keep their random codes.  Every
-    score is then 64 * k_t up to the rounding of the scales, on both sides.
-    k_t is 0 for t < 1500, in {11, 12, 13} up to t < 3500 and in {28, 29, 30}
-    after, so with 1024-token chunks the chunks holding t = 1500 and t = 3500
-    see scores far above the reference their first tile set.
+    As in the bf16 case the absorbed query is exactly 64 * e_0, stored exactly
+    as the e4m3 code 256 with the power-of-two row scale 2^-2.  Latent dim 0 of token t
+    holds k_t: code 448 with token scale k_t / 448 where k_t > 0, code 0
+    (scale as generated) where k_t = 0; the other dims keep their random
+    codes.  Every score is then 64 * k_t up to the rounding of the scales, on
+    both sides.  k_t is 0 for t < 1500, in {11, 12, 13} up to t < 3500 and in
+    the range `late` after, so with 1024-token chunks the chunk holding
+    t = 3500 sees scores far above the reference its first tile set: with
+    {28, 29, 30} up to ~100 log2 units, which the per-tile block exponents
+    absorb in one pass; with {60, 61, 62} more than 300, past the exponent
+    range, so that the kernel takes its second pass with the true row maxima.
     """
     from oracle.codecs import f64_to_e4m3_bits
     spec = inputs.workload(4)
@@ -210,7 +214,7 @@ def test_score_jumps_force_second_pass_fp8_cache():
     for b, L in enumerate(wl.seqlens):
         t = np.arange(int(L))
         k = np.where(t < 1500, 0, np.where(t < 3500, rng.integers(11, 14, t.size),
-                                           rng.integers(28, 31, t.size)))
+                                           rng.integers(late[0], late[1], t.size)))
         pg, sl = wl.block_table[b, t // spec.page_size], t % spec.page_size
         lat[pg, sl, 0] = np.where(k > 0, c448, 0).astype(np.uint8)
         sc[pg, sl] = np.where(k > 0, k / 448.0, sc[pg, sl]).astype(np.float32)

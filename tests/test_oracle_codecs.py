@@ -60,30 +60,29 @@ def test_e4m3_saturates():
 
 def test_row_quantiser_matches_torch_cast_and_bounds():
     """kernel_models.quantize_rows_e4m3 (the fp8 path's query rounding, a kernel
-    model, not part of the oracle): codes equal torch's float8_e4m3fn cast of row / (max|row|/448),
-    the row maximum is kept exactly, and every other value is within half an e4m3 step."""
+    model, not part of the oracle): the scale is the smallest power of two 2^k with
+    max|row| / 2^k <= 448, codes equal torch's float8_e4m3fn cast of row / 2^k (an
+    exact division), and every value is within half an e4m3 step."""
     rng = np.random.default_rng(2)
     x = rng.standard_normal((64, 512)) * np.exp(rng.uniform(-8, 8, (64, 1)))
     x[3] = 0.0
     x[5, 7] = -abs(x[5]).max() * 2          # a negative row maximum
+    x[9] *= 448.0 / np.abs(x[9]).max()      # a row maximum of exactly 448 keeps scale 1
     import kernel_models
     got = kernel_models.quantize_rows_e4m3(x)
     amax = np.abs(x).max(axis=1, keepdims=True)
-    scale = np.where(amax > 0, amax / 448.0, 1.0)
-    codes = torch.from_numpy((x / scale).astype(np.float32)).to(torch.float8_e4m3fn)
+    k = np.ceil(np.log2(np.where(amax > 0, amax, 448.0) / 448.0))
+    scale = np.where(amax > 0, 2.0 ** k, 1.0)
+    assert scale[9, 0] == 1.0
+    y = x / scale
+    # the row maximum lands in (224, 448]
+    assert np.all((np.abs(y).max(axis=1) > 224) | (amax[:, 0] == 0))
+    assert np.all(np.abs(y).max(axis=1) <= 448)
+    codes = torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn)
     ref = codes.double().numpy() * scale
-    # the float32 rounding of x / scale can move a value across a rounding midpoint only
-    # when it sits within float32 precision of one; allow those few
-    mism = got != ref
-    assert mism.mean() < 1e-3
-    assert np.all(np.abs(got[mism] - ref[mism]) <= 32.0 / 448.0 * amax.repeat(512, 1)[mism])
-    # the row maximum is kept (to fp64 rounding of the scale), all-zero rows stay zero
-    idx = np.argmax(np.abs(x), axis=1)
-    mx = x[np.arange(64), idx]
-    assert np.all(np.abs(got[np.arange(64), idx] - mx) <= 4e-16 * np.abs(mx))
+    assert np.array_equal(got, ref)
     assert np.all(got[3] == 0)
     # RNE bound: normal range relative error <= 2^-4; subnormal range absolute <= 2^-10 * scale
-    y = x / scale
     err = np.abs(got / scale - y)
     normal = np.abs(y) >= 2.0 ** -6
     assert np.all(err[normal] <= np.abs(y[normal]) * 2.0 ** -4 + 1e-12)
