@@ -146,7 +146,10 @@ __device__ __forceinline__ MLA_LDS uint8_t* stage_base(int st) {
 // the next tile's softmax, which keeps all their LDS operands alive across
 // the output product).  Consecutive MFMAs of one chain accumulate in place;
 // a VALU read of a chain's result must follow mfma_drain() unless a barrier
-// lies between them.
+// lies between them, and every chain's result must be read: the compiler
+// takes an asm output as written when the asm issues and would reuse the
+// registers of an unread one at once, while the MFMA still runs and writes
+// them later.
 //   latent: e4m3 x e4m3, A unscaled (E8M0 127 = 2^0), B (the query) scaled by
 //   the row's 2^Eq
 __device__ __forceinline__ void mfma_lat_first(f32x16& d, const i32x8& a, const i32x8& b,
@@ -195,15 +198,15 @@ struct TileCopy {
   const uint8_t* lat;
   const uint8_t* rope;
   const float* scale;
-  int tok0, last, st;
+  int lim, st;     // tile rows past lim re-read row lim (31 for a full tile)
 };
 
 __device__ __forceinline__ TileCopy tile_copy(const DecodeArgs& a, int page, int len, int k,
                                               int st) {
   TileCopy c;
-  c.tok0 = k * kTile;
-  c.last = len - 1;
-  const int64_t row0 = (int64_t)page * kPage + (c.tok0 % kPage);
+  const int tok0 = k * kTile;
+  c.lim = uni(min(len - 1 - tok0, kTile - 1));
+  const int64_t row0 = (int64_t)page * kPage + (tok0 % kPage);
   c.lat = (const uint8_t*)a.kv_lat + row0 * LAT_ROW;
   c.rope = (const uint8_t*)a.kv_rope + row0 * ROPE_ROW;
   c.scale = a.kv_scale + row0;
@@ -217,12 +220,12 @@ __device__ __forceinline__ void issue_part(const TileCopy& c, int j, int w, int 
     // lane l fills row 8w + 2j + (l >> 5), slot l & 15 of group (l >> 4) & 1,
     // which holds chunk ((l >> 4) & 1) * 16 + ((l & 15) ^ key)
     const int t = w * 8 + 2 * j + (lane >> 5);
-    const int tc = min(c.tok0 + t, c.last) - c.tok0;
+    const int tc = min(t, c.lim);
     const uint32_t off = (uint32_t)(tc * LAT_ROW + (((lane & 31) ^ lat_key(t)) << 4));
     dma16_s(c.lat, off, dst + (w * 8 + 2 * j) * LAT_ROW);
   } else if (j == 4) {
     const int t = w * 8 + (lane >> 3);
-    const int tc = min(c.tok0 + t, c.last) - c.tok0;
+    const int tc = min(t, c.lim);
     const uint32_t off = (uint32_t)(tc * ROPE_ROW + (((lane & 7) ^ rope_key(t)) << 4));
     dma16_s(c.rope, off, dst + ROPE_OFF + w * 8 * ROPE_ROW);
   } else {
@@ -372,11 +375,13 @@ struct Softmax {
         pin(v[4 * g + r]);
       }
     } else if constexpr (J == 5) {
-      const float m0 = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-      const float m1 = fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7]));
-      const float m2 = fmaxf(fmaxf(v[8], v[9]), fmaxf(v[10], v[11]));
-      const float m3 = fmaxf(fmaxf(v[12], v[13]), fmaxf(v[14], v[15]));
-      mx = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+      // (a tree of three-input maxima)
+      const float m0 = fmaxf(fmaxf(v[0], v[1]), v[2]);
+      const float m1 = fmaxf(fmaxf(v[3], v[4]), v[5]);
+      const float m2 = fmaxf(fmaxf(v[6], v[7]), v[8]);
+      const float m3 = fmaxf(fmaxf(v[9], v[10]), v[11]);
+      const float m4 = fmaxf(fmaxf(v[12], v[13]), v[14]);
+      mx = fmaxf(fmaxf(fmaxf(m0, m1), m2), fmaxf(fmaxf(m3, m4), v[15]));
       pin(mx);
     } else if constexpr (J == 6) {
       // the row's tile maximum: the other half-wave holds the row's other 16
@@ -420,17 +425,18 @@ struct Softmax {
     } else if constexpr (J == 12 || J == 13) {
       // l += P' 2^e / s_t over the lane's tokens (the scaled conversion gives
       // P' 2^e exactly)
-      float acc = 0.f;
+      // (four independent partial sums: no long dependent chain)
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int g = 2 * (J - 12); g < 2 * (J - 12) + 2; ++g) {
         const f32x2 b01 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pk[g], sc, false);
         const f32x2 b23 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pk[g], sc, true);
-        acc = fmaf(b01[0], fv[g][0], acc);
-        acc = fmaf(b01[1], fv[g][1], acc);
-        acc = fmaf(b23[0], fv[g][2], acc);
-        acc = fmaf(b23[1], fv[g][3], acc);
+        acc[0] = fmaf(b01[0], fv[g][0], acc[0]);
+        acc[1] = fmaf(b01[1], fv[g][1], acc[1]);
+        acc[2] = fmaf(b23[0], fv[g][2], acc[2]);
+        acc[3] = fmaf(b23[1], fv[g][3], acc[3]);
       }
-      S.l += acc;
+      S.l += (acc[0] + acc[1]) + (acc[2] + acc[3]);
       pin(S.l);
     }
   }
@@ -471,13 +477,25 @@ __device__ __forceinline__ void mask_rows(const State& S, f32x16& sr, int tok0, 
 // MFMA and 4 rotary MFMAs, with (SM) the softmax of the previous tile run in
 // slices between them and (COPY) the copies of a later tile issued at steps
 // 0, 2, .. 10.  Operand reads run two steps ahead of their MFMAs.
+struct FirstReads {
+  i32x8 k0, k1;
+};
+
+// the latent operands of a tile's first two score steps, issued as soon as
+// the tile's stage is ready so that their latency overlaps the work before
+// the score step
+__device__ __forceinline__ FirstReads first_reads(int st, LaneOff lo) {
+  const uint32_t bq = lds_addr(stage_base(st)) + lo.qk;
+  return FirstReads{load_k(bq, 0), load_k(bq, 1)};
+}
+
 template <bool SM, bool COPY>
 __device__ __forceinline__ void score_step(State& S, int st, const LTab* tab, f32x16& sl,
                                            f32x16& sr, Softmax& prev, int lane, LaneOff lo,
-                                           const TileCopy& cp, int w) {
+                                           const TileCopy& cp, int w, const FirstReads& fr) {
   const uint32_t bq = lds_addr(stage_base(st)) + lo.qk;
   const uint32_t br = lds_addr(stage_base(st)) + lo.rp;
-  i32x8 ka0 = load_k(bq, 0), ka1 = load_k(bq, 1);
+  i32x8 ka0 = fr.k0, ka1 = fr.k1;
   u16x8 ra0, ra1, bias;
 #pragma unroll
   for (int j = 0; j < NQK; ++j) {
@@ -632,12 +650,13 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
   set_qb();
   build_table(a, 0, k0 * kTile, end, tab0, lane);
   barrier();
+  const FirstReads fr0 = first_reads(0, lo);
 #pragma unroll
   for (int i = 2; i <= AHEAD; ++i) issue_tile(copy_of(i), w, lane);
 
   Softmax sa, sb;   // tiles 2p (its pk, code kept for the pair's product), 2p + 1
   sa.tab = tab0;
-  score_step<false, false>(S, 0, tab0, sa.sl, sa.sr, sb, lane, lo, TileCopy{}, w);
+  score_step<false, false>(S, 0, tab0, sa.sl, sa.sr, sb, lane, lo, TileCopy{}, w, fr0);
   mask_rows(S, sa.sr, k0 * kTile, lane);
   mfma_drain();
   sa.all(S, lane, first);
@@ -645,10 +664,11 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
   {
     wait_vm<(AHEAD - 1) * kDma>();
     barrier();
+    const FirstReads fr = first_reads(1, lo);
     const TileCopy c = copy_of(1 + AHEAD);
     build_table(a, 1, (k0 + 1) * kTile, end, tab1, lane);
     sb.tab = tab1;
-    score_step<false, true>(S, 1, tab1, sb.sl, sb.sr, sa, lane, lo, c, w);
+    score_step<false, true>(S, 1, tab1, sb.sl, sb.sr, sa, lane, lo, c, w, fr);
     mask_rows(S, sb.sr, (k0 + 1) * kTile, lane);
   }
   for (int p = 1; p < np; ++p) {
@@ -658,10 +678,11 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
     {
       wait_vm<(AHEAD - 1) * kDma>();
       barrier();
+      const FirstReads fr = first_reads(i0 % NSTAGE, lo);
       const TileCopy c = copy_of(i0 + AHEAD);
       build_table(a, i0 % NSTAGE, (k0 + i0) * kTile, end, tab0, lane);
       f32x16 nsl, nsr;
-      score_step<true, true>(S, i0 % NSTAGE, tab0, nsl, nsr, sb, lane, lo, c, w);
+      score_step<true, true>(S, i0 % NSTAGE, tab0, nsl, nsr, sb, lane, lo, c, w, fr);
       mask_rows(S, nsr, (k0 + i0) * kTile, lane);
       pv_step(S, sa.pk, sa.code, sb.pk, sb.code, (i0 - 2) % NSTAGE, (i0 - 1) % NSTAGE, lane, lo);
       sa.sl = nsl;
@@ -672,10 +693,11 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
     {
       wait_vm<(AHEAD - 1) * kDma>();
       barrier();
+      const FirstReads fr = first_reads((i0 + 1) % NSTAGE, lo);
       const TileCopy c = copy_of(i0 + 1 + AHEAD);
       build_table(a, (i0 + 1) % NSTAGE, (k0 + i0 + 1) * kTile, end, tab1, lane);
       f32x16 nsl, nsr;
-      score_step<true, true>(S, (i0 + 1) % NSTAGE, tab1, nsl, nsr, sa, lane, lo, c, w);
+      score_step<true, true>(S, (i0 + 1) % NSTAGE, tab1, nsl, nsr, sa, lane, lo, c, w, fr);
       mask_rows(S, nsr, (k0 + i0 + 1) * kTile, lane);
       sb.sl = nsl;
       sb.sr = nsr;
