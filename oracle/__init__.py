@@ -26,7 +26,9 @@ pages it follows:
   section "Three Main Architectures" (RMSNorm of the compressed key/value in
   FP32), for the cache append.
 * [SNAP]  "Related papers: SnapMLA: Efficient Long-Context MLA Decoding via H…"
-  (scifaro.com), the abstract on two functionally equivalent kernel forms.
+  (scifaro.com), the abstract on two functionally equivalent kernel forms, and
+  the abstracts naming cache-eviction techniques (StreamingLLM, SnapKV), for
+  the decode over an evicted cache in ``eviction``.
 
 Floating point is fp64 throughout.  Stored inputs (bf16 / OCP e4m3 bit
 patterns) are decoded by this package's own codecs.
@@ -45,6 +47,7 @@ from .append import (rms_norm, append_positions, quantize_token_e4m3, append_kv,
                      RMS_EPS)
 from .projections import (down_project, up_project_query, absorb_query_weights,
                           absorb_output_weights, output_project)
+from .eviction import streaming_kept, mla_decode_streaming
 from .cache_sizes import (mla_cache_elems_per_token, mha_cache_elems_per_token,
                           gqa_cache_elems_per_token, mqa_cache_elems_per_token,
                           gqa_equivalent_groups)
@@ -56,7 +59,7 @@ __all__ = [
     "decode_stored", "DecodeResult", "inputs_from_workload",
     "rms_norm", "append_positions", "quantize_token_e4m3", "append_kv", "RMS_EPS",
     "down_project", "up_project_query", "absorb_query_weights", "absorb_output_weights",
-    "output_project", "mla_cache_elems_per_token",
+    "output_project", "streaming_kept", "mla_decode_streaming", "mla_cache_elems_per_token",
     "mha_cache_elems_per_token", "gqa_cache_elems_per_token",
     "mqa_cache_elems_per_token", "gqa_equivalent_groups",
 ]
