@@ -303,13 +303,14 @@ def kind_of(spec):
     return "fp8" if spec.latent_dtype == "e4m3" else "bf16"
 
 
-def replicate_cache(db):
+def replicate_cache(db, read_bytes=None):
     """Copies of the cache so that consecutive launches read different copies and
-    together exceed twice the 256 MB last-level cache."""
+    together exceed twice the 256 MB last-level cache (`read_bytes`: the bytes
+    one launch reads, when it reads less than the whole cache)."""
     cache_bytes = db.kv_latent.numel() * db.kv_latent.element_size() \
         + db.kv_rope.numel() * db.kv_rope.element_size() \
         + (db.kv_scale.numel() * 4 if db.kv_scale is not None else 0)
-    n_rep = max(2, math.ceil(2 * MALL_BYTES / cache_bytes))
+    n_rep = max(2, math.ceil(2 * MALL_BYTES / (read_bytes or cache_bytes)))
     reps = [(db.kv_latent, db.kv_scale, db.kv_rope)]
     for _ in range(n_rep - 1):
         reps.append((db.kv_latent.clone(), None if db.kv_scale is None else db.kv_scale.clone(),
@@ -328,20 +329,21 @@ def calibration_copy(mib):
     del src, dst
 
 
-def time_decode(db, reps, launches, warm=10):
+def time_decode(db, reps, launches, warm=10, **view):
     """Durations (ms) of `launches` back-to-back decode launches, each bracketed
-    by HIP events on the launch stream, rotating over the cache replicas."""
+    by HIP events on the launch stream, rotating over the cache replicas
+    (`view`: block_table, seqlens, max_seqlen of an eviction view)."""
     import torch
     stream = torch.cuda.current_stream()
     for i in range(warm):
         lat, sc, rope = reps[i % len(reps)]
-        db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope)
+        db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope, **view)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(launches)]
     for i, (a, b) in enumerate(ev):
         lat, sc, rope = reps[i % len(reps)]
         a.record(stream)
-        db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope)
+        db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope, **view)
         b.record(stream)
     torch.cuda.synchronize()
     return np.array([a.elapsed_time(b) for a, b in ev])
@@ -395,6 +397,45 @@ def decode_object(cfg, launches, copy_mib=0):
     out = decode_roofline(spec, wl.seqlens, ms, read_traffic(kind_of(spec), spec.name))
     out["cache_replicas"] = len(reps)
     out["tokens_in_cache"] = int(wl.tokens)
+    out["batch"], out["q_len"] = spec.batch, spec.q_len
+    del reps, db
+    torch.cuda.empty_cache()
+    return out
+
+
+def streaming_object(launches, sink_pages=1, window_pages=64):
+    """Decode over the StreamingLLM-style eviction view of the long-context
+    workload (B=16, L uniform in 16K..64K): 1 sink page and a recent window of
+    at least 64 pages (4096 tokens) kept per sequence.  Times the view kernel
+    and the decode over the kept pages; the roofline is over the kept tokens'
+    bytes (cache replicated until the kept pages exceed twice the last-level
+    cache)."""
+    import torch
+    from head_latent_attention_03_amd import inputs
+    from head_latent_attention_03_amd.runner import DeviceBatch
+    spec = inputs.workload(3)
+    wl = inputs.make_workload(spec)
+    db = DeviceBatch.from_workload(wl, "cuda:0")
+    db.absorb()
+    sl, bt, ms_view = db.streaming_view(sink_pages, window_pages)
+    torch.cuda.synchronize()
+    kept = sl.cpu().numpy()
+    per_tok = spec.d_c * 2 + spec.d_rope * 2
+    reps = replicate_cache(db, read_bytes=int(kept.sum()) * per_tok)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        db.streaming_view(sink_pages, window_pages)
+    e1.record()
+    torch.cuda.synchronize()
+    view_us = e0.elapsed_time(e1) / 20 * 1e3
+    ms = time_decode(db, reps, launches, block_table=bt, seqlens=sl, max_seqlen=ms_view)
+    out = decode_roofline(spec, kept, ms, None)
+    out["workload"] = spec.name + "-streaming-sink1-win64"
+    out["tokens_kept"] = int(kept.sum())
+    out["tokens_in_cache"] = int(wl.tokens)
+    out["view_kernel_us"] = round(view_us, 2)
+    out["cache_replicas"] = len(reps)
     out["batch"], out["q_len"] = spec.batch, spec.q_len
     del reps, db
     torch.cuda.empty_cache()
@@ -632,7 +673,8 @@ def cpu_baseline(wl, budget_s):
 
 
 EXTRA_WORKLOADS = {"e4m3_cache": 4, "long_context": 3, "mtp2": 5, "prefill": "prefill",
-                   "projection": "projection", "e4m3_second_pass": "second_pass"}
+                   "projection": "projection", "e4m3_second_pass": "second_pass",
+                   "streaming_eviction": "streaming"}
 
 
 def main():
@@ -644,12 +686,13 @@ def main():
     ap.add_argument("--decode-launches", type=int, default=50,
                     help="decode launches timed one by one for each roofline object")
     ap.add_argument("--extra", default="e4m3_cache,long_context,mtp2,prefill,projection,"
-                                       "e4m3_second_pass",
+                                       "e4m3_second_pass,streaming_eviction",
                     help="comma-separated decode-only objects for the other workloads "
                          f"({', '.join(EXTRA_WORKLOADS)}; empty: none)")
     ap.add_argument("--decode-only", type=int, default=0, metavar="N",
                     help="time only the decode of workload N (for profiling runs) and exit")
-    ap.add_argument("--object", choices=["prefill", "projection", "e4m3_second_pass"],
+    ap.add_argument("--object", choices=["prefill", "projection", "e4m3_second_pass",
+                                         "streaming_eviction"],
                     help="time only this extra object (for profiling runs) and exit")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0: skip)")
@@ -694,6 +737,8 @@ def main():
             obj = prefill_object(max(5, args.decode_launches // 5))
         elif args.object == "projection":
             obj = projection_object(max(10, args.decode_launches // 2))
+        elif args.object == "streaming_eviction":
+            obj = streaming_object(args.decode_launches)
         else:
             obj = fp8_second_pass_object(max(10, args.decode_launches // 2),
                                          torch.cuda.get_device_properties(0).multi_processor_count)
@@ -783,6 +828,8 @@ def main():
                 out[name] = prefill_object(max(5, args.decode_launches // 5))
             elif EXTRA_WORKLOADS[name] == "projection":
                 out[name] = projection_object(max(10, args.decode_launches // 2))
+            elif EXTRA_WORKLOADS[name] == "streaming":
+                out[name] = streaming_object(args.decode_launches)
             elif EXTRA_WORKLOADS[name] == "second_pass":
                 out[name] = fp8_second_pass_object(max(10, args.decode_launches // 2),
                                                    torch.cuda.get_device_properties(0).multi_processor_count)

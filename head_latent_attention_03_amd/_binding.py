@@ -95,6 +95,8 @@ def load_library(path=LIBRARY_PATH):
     lib.mla_append_kv.argtypes = [dp, i32, i32, _P, _P, _P, ctypes.c_float, i32p, i32p, i32,
                                   _P, _P, _P, i32, _P]
     lib.mla_append_kv.restype = ctypes.c_int
+    lib.mla_streaming_view.argtypes = [dp, i32, i32p, i32p, i32, i32, i32, i32p, i32p, i32, _P]
+    lib.mla_streaming_view.restype = ctypes.c_int
     lib.mla_validate_paged_host.argtypes = [dp, i32, i32, _P, i32, _P, i32,
                                             ctypes.POINTER(ctypes.c_int32)]
     lib.mla_validate_paged_host.restype = ctypes.c_int
@@ -274,6 +276,23 @@ def mla_append_kv(dims, kv_c, k_rope, norm_weight, norm_eps, seqlens, block_tabl
         ctypes.byref(d), B, S, _ptr(kv_c), _ptr(k_rope), _ptr(norm_weight), float(norm_eps),
         _ptr(seqlens), _ptr(block_table), block_table.shape[1], _ptr(kv_latent),
         _ptr(kv_scale), _ptr(kv_rope), P, _stream(stream)))
+
+
+def mla_streaming_view(dims, seqlens, block_table, sink_pages, window_pages, out_seqlens,
+                       out_block_table, stream=None):
+    """The eviction view (kept sink pages and recent window) of a paged cache as new
+    lengths and a new block table; see mla_streaming_view in mla_decode.h."""
+    B = seqlens.shape[0]
+    dev = seqlens.device
+    _expect("seqlens", seqlens, (B,), torch.int32, dev)
+    _expect("block_table", block_table, (B, block_table.shape[1]), torch.int32, dev)
+    _expect("out_seqlens", out_seqlens, (B,), torch.int32, dev)
+    _expect("out_block_table", out_block_table, (B, out_block_table.shape[1]), torch.int32, dev)
+    d = dims.c()
+    _check("mla_streaming_view", load_library().mla_streaming_view(
+        ctypes.byref(d), B, _ptr(seqlens), _ptr(block_table), block_table.shape[1],
+        int(sink_pages), int(window_pages), _ptr(out_seqlens), _ptr(out_block_table),
+        out_block_table.shape[1], _stream(stream)))
 
 
 def mla_decode_noalloc(dims, q_latent, q_latent_scale, q_pe, kv_latent, kv_scale, kv_rope,

@@ -319,6 +319,33 @@ MLA_EXPORT mla_status_t mla_decode_paged(const mla_dims_t* dims, int32_t batch, 
   return launch_status(e);
 }
 
+MLA_EXPORT mla_status_t mla_streaming_view(const mla_dims_t* dims, int32_t batch,
+                                           const int32_t* seqlens, const int32_t* block_table,
+                                           int32_t max_pages_per_seq, int32_t sink_pages,
+                                           int32_t window_pages, int32_t* out_seqlens,
+                                           int32_t* out_block_table, int32_t max_pages_out,
+                                           void* stream) {
+  mla_status_t st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || max_pages_per_seq < 1 || sink_pages < 0 || window_pages < 1 ||
+      max_pages_out < sink_pages + window_pages + 1)
+    return MLA_ERR_BAD_SHAPE;
+  if (!seqlens || !block_table || !out_seqlens || !out_block_table) return MLA_ERR_NULL_POINTER;
+  if (batch == 0) return MLA_OK;
+  mla::StreamingViewArgs a;
+  a.seqlens = seqlens;
+  a.block_table = block_table;
+  a.out_seqlens = out_seqlens;
+  a.out_block_table = out_block_table;
+  a.batch = batch;
+  a.max_pages = max_pages_per_seq;
+  a.max_pages_out = max_pages_out;
+  a.page_size = dims->page_size;
+  a.sink_pages = sink_pages;
+  a.window_pages = window_pages;
+  return launch_status(mla::launch_streaming_view(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 MLA_EXPORT mla_status_t mla_append_kv(const mla_dims_t* dims, int32_t batch, int32_t q_len,
                                       const void* kv_c, const void* k_rope,
                                       const void* norm_weight, float norm_eps,

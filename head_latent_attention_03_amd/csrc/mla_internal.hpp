@@ -85,6 +85,16 @@ struct ValidateArgs {
 
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t s);
 
+struct StreamingViewArgs {
+  const int32_t* seqlens;
+  const int32_t* block_table;
+  int32_t* out_seqlens;
+  int32_t* out_block_table;
+  int32_t batch, max_pages, max_pages_out, page_size, sink_pages, window_pages;
+};
+
+hipError_t launch_streaming_view(const StreamingViewArgs& a, hipStream_t s);
+
 struct GemmArgs {            // C[b] = A[b] B[b]^T, bf16 in, fp32 accumulate
   const void* a;             // [batch][m][lda] bf16 (k contiguous)
   const void* b;             // [batch][n][ldb] bf16 (k contiguous)

@@ -94,22 +94,36 @@ class DeviceBatch:
                        self.q_latent, self.q_latent_scale, self.q_pe, stream=stream)
 
     def decode(self, kv_latent=None, kv_scale=None, kv_rope=None, block_table=None,
-               stream=None):
+               stream=None, seqlens=None, max_seqlen=None):
         B.mla_decode_paged(self.dims, self.q_latent, self.q_latent_scale, self.q_pe,
                            self.kv_latent if kv_latent is None else kv_latent,
                            self.kv_scale if kv_scale is None else kv_scale,
                            self.kv_rope if kv_rope is None else kv_rope,
                            self.block_table if block_table is None else block_table,
-                           self.seqlens, self.max_seqlen, self.workspace, causal=self.causal,
-                           stream=stream)
+                           self.seqlens if seqlens is None else seqlens,
+                           self.max_seqlen if max_seqlen is None else max_seqlen,
+                           self.workspace, causal=self.causal, stream=stream)
 
-    def combine(self, with_uv=True, stream=None):
+    def combine(self, with_uv=True, stream=None, seqlens=None, max_seqlen=None):
+        sl = self.seqlens if seqlens is None else seqlens
+        ms = self.max_seqlen if max_seqlen is None else max_seqlen
         if with_uv:
-            B.mla_combine(self.dims, self.workspace, self.seqlens, self.max_seqlen, self.w_uv,
+            B.mla_combine(self.dims, self.workspace, sl, ms, self.w_uv,
                           self.out, self.lse, q_len=self.q_len, stream=stream)
         else:
-            B.mla_combine(self.dims, self.workspace, self.seqlens, self.max_seqlen, None,
+            B.mla_combine(self.dims, self.workspace, sl, ms, None,
                           self.out_latent, self.lse, q_len=self.q_len, stream=stream)
+
+    def streaming_view(self, sink_pages, window_pages, stream=None):
+        """The eviction view of this batch's cache (mla_streaming_view): returns
+        (seqlens, block_table, max_seqlen) to pass to decode() and combine(); the
+        absorb keeps the true lengths."""
+        cols = sink_pages + window_pages + 1
+        sl = torch.empty_like(self.seqlens)
+        bt = torch.empty((self.batch, cols), dtype=torch.int32, device=self.seqlens.device)
+        B.mla_streaming_view(self.dims, self.seqlens, self.block_table, sink_pages, window_pages,
+                             sl, bt, stream=stream)
+        return sl, bt, min(self.max_seqlen, cols * self.dims.page_size)
 
     def step(self, with_uv=True, stream=None):
         """One decode step: absorb, paged split-KV attention, combine."""

@@ -185,6 +185,39 @@ mla_status_t mla_combine(const mla_dims_t* dims, int32_t batch, int32_t q_len,
                          const void* w_uv, void* out, float* lse, void* stream);
 
 /*
+ * StreamingLLM-style eviction view of the paged cache (the related-papers
+ * page "Related papers: SnapMLA: Efficient Long-Context MLA Decoding via H…",
+ * scifaro.com, names such eviction techniques, StreamingLLM and SnapKV, for
+ * bounding a long context's KV cache).  A sequence of L tokens keeps its first
+ * sink_pages pages and its most recent tokens from the page boundary at or
+ * below L - window_pages * page_size on; a sequence whose window would reach
+ * back into its sinks keeps everything.  Kept tokens are not moved and keep
+ * the positions they were cached at; the view is a new block table and new
+ * lengths, written on the device:
+ *   out_seqlens[b]      = tokens kept (sink_pages * page_size + L - start, or L)
+ *   out_block_table[b]  = the kept pages in order (sink pages, then window
+ *                         pages), 0 in the unused columns
+ * A decode step over the view runs mla_absorb_q with the TRUE seqlens (the
+ * query positions), then mla_decode_paged and mla_combine with out_seqlens,
+ * out_block_table, max_pages_out and a max_seqlen of at most
+ * max_pages_out * page_size; every kept token's score is its score in the full
+ * cache, so the result is attention restricted to the kept keys.
+ *   seqlens, block_table [batch, max_pages_per_seq]   as for mla_decode_paged
+ *   sink_pages >= 0, window_pages >= 1
+ *   out_seqlens [batch] int32, out_block_table [batch, max_pages_out] int32:
+ *     device, written; max_pages_out >= sink_pages + window_pages + 1
+ * Errors: MLA_ERR_BAD_SHAPE for counts out of range, MLA_ERR_NULL_POINTER,
+ * MLA_ERR_HIP for a failed launch.  The same device preconditions as the
+ * decode apply to seqlens and block_table.
+ */
+mla_status_t mla_streaming_view(const mla_dims_t* dims, int32_t batch,
+                                const int32_t* seqlens, const int32_t* block_table,
+                                int32_t max_pages_per_seq, int32_t sink_pages,
+                                int32_t window_pages, int32_t* out_seqlens,
+                                int32_t* out_block_table, int32_t max_pages_out,
+                                void* stream);
+
+/*
  * Append the new tokens of a decode step to the paged cache (run it before
  * the step's mla_decode_paged).  New token j of sequence b sits at position
  * pos = seqlens[b] - q_len + j (the lengths already count the new tokens);

@@ -72,11 +72,15 @@ def mla_decode_streaming(inputs, sink_tokens, window_tokens, rows=None):
     out = np.zeros((n, d_v))
     o_lat = np.zeros((n, d_c))
     lse = np.full(n, -np.inf)
+    gathered = {}
     for i, (b, j, h) in enumerate(rows):
         b, j, h = int(b), int(j), int(h)
         length = int(seqlens[b])
-        c, kr = gather_cache(inputs["kv_latent"], inputs["kv_rope"], inputs["block_table"],
-                             b, length, page)
+        if b not in gathered:
+            # (one sequence's cache at a time)
+            gathered = {b: gather_cache(inputs["kv_latent"], inputs["kv_rope"],
+                                        inputs["block_table"], b, length, page)}
+        c, kr = gathered[b]
         pos = length - q_len + j
         kept = streaming_kept(length, sink_tokens, window_tokens, page)
         if causal:

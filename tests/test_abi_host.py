@@ -210,3 +210,17 @@ def test_gemm_and_weight_absorption_argument_checks(lib):
     assert qf(ql=NULL) == 1
     assert qf(q_len=9) == 2
     assert qf(dims=_dims(latent_dtype="e4m3")) == 6
+
+
+def test_streaming_view_argument_checks(lib):
+    """mla_streaming_view answers bad counts and null pointers from the host (no device
+    call): sink_pages >= 0, window_pages >= 1, max_pages_out >= sink + window + 1."""
+    d = _dims()
+    call = lambda **kw: lib.mla_streaming_view(
+        ctypes.byref(d), kw.get("batch", 2), kw.get("sl", A16), A16, kw.get("max_pages", 8),
+        kw.get("sink", 1), kw.get("window", 4), kw.get("osl", A16), kw.get("obt", A16),
+        kw.get("cols", 6), NULL)
+    assert call(sl=NULL) == 1 and call(osl=NULL) == 1 and call(obt=NULL) == 1
+    assert call(sink=-1) == 2 and call(window=0) == 2
+    assert call(cols=5) == 2 and call(max_pages=0) == 2 and call(batch=-1) == 2
+    assert call(batch=0) == 0
