@@ -411,12 +411,13 @@ __device__ __forceinline__ void probs(const DecodeArgs& a, State& S, const f32x1
 
 // One pass over the chunk's tiles [k0, k0 + n).  Iteration i (0 <= i <= n)
 // runs the output product of tile i - 1 and the scores of tile i.
-// The pass starts by copying tiles 0 and 1 and calling `loads`, which issues
-// NLOADS vector loads (the query, on the first pass).  Tile 0 is waited for
-// alone; the compiler waits for each loaded register where the first scores
-// use it, so those start before the loads have all landed.  Tile 2 is copied
-// after them: a copy issued earlier would sit among the loads the compiler
-// counts and hold up those waits.
+// The pass starts by calling `loads`, which issues NLOADS vector loads (the
+// query, on the first pass) right after the block-table read, so that their
+// latency overlaps that read's; then it copies tiles 0 and 1.  Tile 0 is
+// waited for alone, and the loads, issued before it, have landed with it
+// (the compiler's own waits for their registers can still count tile 1's
+// copies, which are younger, but those land right behind tile 0's).  Tile 2
+// is copied after the first scores.
 template <int NLOADS, typename Loads>
 __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Chunk& ch, int k0,
                                          int n, int w, int lane, Loads loads) {
@@ -434,10 +435,10 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
     const int page = page_lookup(W, bt_row, a.max_pages, k * kTile / kPage, lane);
     return tile_copy(a, page, ch.len, k, st);
   };
+  loads();
   issue_tile(copy_of(k0, 0), w, lane);
   issue_tile(copy_of(k0 + 1, 1), w, lane);
-  loads();
-  wait_vm<kDma + NLOADS>();
+  wait_vm<kDma>();
   barrier();
 
   // Iteration i (1 <= i < n) waits for tile i (this wave's copies are done
@@ -564,9 +565,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_bf16_kernel(DecodeArgs a) 
   S.lim = valid ? (a.causal ? ch.len - a.q_len + jq + 1 : ch.len) : 0;
   S.tmax = -INFINITY;
   S.redo = false;
-  // the query (KS vector loads per lane, issued right after the first two
-  // tiles' copies); lane (hh, lc) holds dims 16ks + 8hh .. +7 of its row for
-  // every k-step ks
+  // the query (KS vector loads per lane, issued right after the block-table
+  // read); lane (hh, lc) holds dims 16ks + 8hh .. +7 of its row for every
+  // k-step ks
   auto load_query = [&]() {
     const int64_t qrow = ((int64_t)ch.b * a.q_len + jq) * a.n_heads + hq;
 #pragma unroll

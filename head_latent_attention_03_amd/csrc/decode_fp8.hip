@@ -576,10 +576,11 @@ __device__ __forceinline__ void pv_step(State& S, const uint32_t (&pa)[4], int c
 
 // The chunk's one pass over its tiles [k0, k0 + n), as pairs (a last odd
 // tile pairs with a phantom tile whose keys all lie past the chunk end).
-//   * Prologue: the page window, the copies of tiles 0 and 1 and the query,
-//     all landed before the first barrier (the query registers are marked
-//     used there, so that no wait the compiler places for its own loads can
-//     fall behind a later copy), then tiles 2 .. AHEAD.  Tile 0's scores and
+//   * Prologue: the page window, the query (issued before the window has
+//     landed, so that the two latencies overlap) and the copies of tiles 0
+//     and 1, all landed before the first barrier (the query registers are
+//     marked used there, so that no wait the compiler places for its own
+//     loads can fall behind a later copy), then tiles 2 .. AHEAD.  Tile 0's scores and
 //     softmax set each row's reference m (first pass); tile 1's scores
 //     follow.
 //   * Tile i (i >= 1): wait for it (this wave's copies are done once at most
@@ -621,9 +622,9 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
                        : __builtin_bit_cast(u16x8, u32x4{kOneBf16 | (kOneBf16 << 16), mneg, 0u, 0u});
   };
 
+  if (first) load_query();
   issue_tile(copy_of(0), w, lane);
   issue_tile(copy_of(1), w, lane);
-  if (first) load_query();
   wait_vm<0>();
   if (first) {
 #pragma unroll
