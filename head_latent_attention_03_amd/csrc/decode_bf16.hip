@@ -159,6 +159,25 @@ __device__ __forceinline__ void issue_part(const TileCopy& c, int j, int w, int 
   }
 }
 
+// Entries pg and pg + 1 of a block-table row (clamped to its max_pages
+// entries) through the scalar cache, waited for in place.  The wait counts
+// scalar loads only: it neither holds on the vector loads in flight nor
+// leaves the compiler a vector load to wait for, whose wait would count every
+// older vector load and copy (so that the first tiles' copies would go out
+// one tile at a time).
+__device__ __forceinline__ void scalar_table_entries2(const int32_t* row, int pg, int max_pages,
+                                                      int (&out)[2]) {
+  const int32_t* p0 = row + min(pg, max_pages - 1);
+  const int32_t* p1 = row + min(pg + 1, max_pages - 1);
+  int v0, v1;
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(v0), "=&s"(v1)
+               : "s"(p0), "s"(p1)
+               : "memory");
+  out[0] = v0;
+  out[1] = v1;
+}
+
 __device__ __forceinline__ void issue_tile(const TileCopy& c, int w, int lane) {
 #pragma unroll
   for (int j = 0; j < kDma; ++j) issue_part(c, j, w, lane);
@@ -425,7 +444,6 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
   const int32_t* bt_row = a.block_table + (int64_t)ch.b * a.max_pages;
   PageWindow W;
   W.pg0 = uni(k0 * kTile / kPage);
-  W.v = page_window_load(bt_row, a.max_pages, W.pg0, lane);
   // every iteration copies one tile, so that the copy count (and with it each
   // vmcnt wait) is the same on every path; a copy past the chunk's last tile
   // re-reads that tile into a stage that is not read again
@@ -435,10 +453,21 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
     const int page = page_lookup(W, bt_row, a.max_pages, k * kTile / kPage, lane);
     return tile_copy(a, page, ch.len, k, st);
   };
+  // the first tiles' pages through the scalar cache (tiles 0 .. 2 lie in
+  // pages pg0 and pg0 + 1), then the page window of the later tiles
+  static_assert((3 * kTile) / kPage <= 2, "prologue pages");
   loads();
-  issue_tile(copy_of(k0, 0), w, lane);
-  issue_tile(copy_of(k0 + 1, 1), w, lane);
-  wait_vm<kDma>();
+  int pgs[2];
+  scalar_table_entries2(bt_row, W.pg0, a.max_pages, pgs);
+  auto prologue_copy = [&](int k, int st) {
+    k = min(k, k_last);
+    const int page = uni(k * kTile / kPage - W.pg0) == 0 ? pgs[0] : pgs[1];
+    return tile_copy(a, page, ch.len, k, st);
+  };
+  issue_tile(prologue_copy(k0, 0), w, lane);
+  issue_tile(prologue_copy(k0 + 1, 1), w, lane);
+  W.v = page_window_load(bt_row, a.max_pages, W.pg0, lane);
+  wait_vm<kDma + 1>();
   barrier();
 
   // Iteration i (1 <= i < n) waits for tile i (this wave's copies are done
@@ -449,7 +478,11 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
   u16x8 p[2];
   f32x16 sacc;
   tile_step<true, false, false>(S, 0, 0, p, lane, lo, TileCopy{}, w, sacc);
-  issue_tile(copy_of(k0 + 2, 2), w, lane);
+  // (the page window is needed from iteration 1 on: waiting for it here, with
+  // tile 1, keeps the compiler's wait out of the loop, where it would count
+  // the copies of later tiles)
+  asm volatile("" ::"v"(W.v));
+  issue_tile(prologue_copy(k0 + 2, 2), w, lane);
   set_reference(a, S, sacc, k0 * kTile, lane);
   probs<true>(a, S, sacc, k0 * kTile, lane, p);
   // Iterations 1 .. n_fast - 1 take the fast path: their tile has no key at

@@ -141,6 +141,31 @@ __device__ __forceinline__ MLA_LDS uint8_t* stage_base(int st) {
   return (MLA_LDS uint8_t*)s_ring + st * STAGE;
 }
 
+// Entries pg .. pg + 3 of a block-table row (clamped to its max_pages
+// entries) through the scalar cache, waited for in place.  The wait counts
+// scalar loads only: it neither holds on the vector loads in flight nor
+// leaves the compiler a vector load to wait for, whose wait would count
+// every older vector load and copy (so that the prologue's copies would go
+// out one tile at a time).
+__device__ __forceinline__ void scalar_table_entries4(const int32_t* row, int pg, int max_pages,
+                                                      int (&out)[4]) {
+  const int32_t* p0 = row + min(pg, max_pages - 1);
+  const int32_t* p1 = row + min(pg + 1, max_pages - 1);
+  const int32_t* p2 = row + min(pg + 2, max_pages - 1);
+  const int32_t* p3 = row + min(pg + 3, max_pages - 1);
+  int v0, v1, v2, v3;
+  asm volatile(
+      "s_load_dword %0, %4, 0x0\n\ts_load_dword %1, %5, 0x0\n\t"
+      "s_load_dword %2, %6, 0x0\n\ts_load_dword %3, %7, 0x0\n\ts_waitcnt lgkmcnt(0)"
+      : "=&s"(v0), "=&s"(v1), "=&s"(v2), "=&s"(v3)
+      : "s"(p0), "s"(p1), "s"(p2), "s"(p3)
+      : "memory");
+  out[0] = v0;
+  out[1] = v1;
+  out[2] = v2;
+  out[3] = v3;
+}
+
 // The score MFMAs, written as volatile asm so that each stays in the step it
 // is issued in (as pure builtins the compiler sinks them toward their use in
 // the next tile's softmax, which keeps all their LDS operands alive across
@@ -604,7 +629,6 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
   const int32_t* bt_row = a.block_table + (int64_t)ch.b * a.max_pages;
   PageWindow W;
   W.pg0 = uni(k0 * kTile / kPage);
-  W.v = page_window_load(bt_row, a.max_pages, W.pg0, lane);
   const int k_last = k0 + n - 1;
   const int np = (n + 1) >> 1;
   const int end = min(ch.len, (k0 + n) * kTile);   // keys at or past end are masked
@@ -622,15 +646,30 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
                        : __builtin_bit_cast(u16x8, u32x4{kOneBf16 | (kOneBf16 << 16), mneg, 0u, 0u});
   };
 
+  // the prologue's tiles 0 .. AHEAD + 1 lie in pages pg0 .. pg0 + 3
+  static_assert(((AHEAD + 1) * kTile) / kPage + 1 <= 4, "prologue pages");
   if (first) load_query();
-  issue_tile(copy_of(0), w, lane);
-  issue_tile(copy_of(1), w, lane);
+  int pgs[4];
+  scalar_table_entries4(bt_row, W.pg0, a.max_pages, pgs);
+  auto prologue_copy = [&](int i) {
+    const int k = min(k0 + i, k_last);
+    const int d = uni(k * kTile / kPage - W.pg0);
+    const int page = d == 0 ? pgs[0] : (d == 1 ? pgs[1] : (d == 2 ? pgs[2] : pgs[3]));
+    return tile_copy(a, page, ch.len, k, i % NSTAGE);
+  };
+  issue_tile(prologue_copy(0), w, lane);
+  issue_tile(prologue_copy(1), w, lane);
+  // the page window of the later tiles, landed with the copies
+  W.v = page_window_load(bt_row, a.max_pages, W.pg0, lane);
   wait_vm<0>();
+  pin(W.v);
   if (first) {
 #pragma unroll
     for (int kk = 0; kk < KS_LAT; ++kk) asm volatile("" ::"v"(S.q8[kk]));
 #pragma unroll
     for (int kk = 0; kk < KS_ROPE; ++kk) asm volatile("" ::"v"(S.qpe[kk]));
+    // (the row scale's exponent field is its E8M0 code)
+    S.qsc = (int)((uint32_t)S.qsc >> 23) & 0xff;
     asm volatile("" ::"v"(S.qsc));
     // the softmax scale (log2 units) goes into the rotary query (rounded to
     // bf16 again: 2^-9 relative on the rotary part of a score)
@@ -653,7 +692,7 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
   barrier();
   const FirstReads fr0 = first_reads(0, lo);
 #pragma unroll
-  for (int i = 2; i <= AHEAD; ++i) issue_tile(copy_of(i), w, lane);
+  for (int i = 2; i <= AHEAD; ++i) issue_tile(prologue_copy(i), w, lane);
 
   Softmax sa, sb;   // tiles 2p (its pk, code kept for the pair's product), 2p + 1
   sa.tab = tab0;
@@ -666,7 +705,7 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
     wait_vm<(AHEAD - 1) * kDma>();
     barrier();
     const FirstReads fr = first_reads(1, lo);
-    const TileCopy c = copy_of(1 + AHEAD);
+    const TileCopy c = prologue_copy(1 + AHEAD);
     build_table(a, 1, (k0 + 1) * kTile, end, tab1, lane);
     sb.tab = tab1;
     score_step<false, true>(S, 1, tab1, sb.sl, sb.sr, sa, lane, lo, c, w, fr);
@@ -789,9 +828,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fp8_kernel(DecodeArgs a) {
     for (int kk = 0; kk < KS_LAT; ++kk) S.q8[kk] = *(const i32x8*)(q8 + kk * 64 + hh * 32);
 #pragma unroll
     for (int kk = 0; kk < KS_ROPE; ++kk) S.qpe[kk] = *(const u16x8*)(qpe + kk * 16 + hh * 8);
-    // the row scale is a power of two (the absorb pass writes it so): its
-    // exponent field is the E8M0 code
-    S.qsc = (int)((__float_as_uint(a.q_scale[qrow]) >> 23) & 0xffu);
+    // the row scale is a power of two (the absorb pass writes it so); its
+    // bits for now, the code once it has landed
+    S.qsc = (int)__float_as_uint(a.q_scale[qrow]);
   };
 
   // the pass, and a rare second one with the true row maxima as references
