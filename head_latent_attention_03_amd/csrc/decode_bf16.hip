@@ -160,17 +160,18 @@ __device__ __forceinline__ void issue_part(const TileCopy& c, int j, int w, int 
 }
 
 // Entries pg and pg + 1 of a block-table row (clamped to its max_pages
-// entries) through the scalar cache, waited for in place.  The wait counts
-// scalar loads only: it neither holds on the vector loads in flight nor
-// leaves the compiler a vector load to wait for, whose wait would count every
-// older vector load and copy (so that the first tiles' copies would go out
-// one tile at a time).
+// entries) by scalar loads, waited for in place.  The wait counts scalar
+// loads only: it neither holds on the vector loads in flight nor leaves the
+// compiler a vector load to wait for, whose wait would count every older
+// vector load and copy (so that the first tiles' copies would go out one tile
+// at a time).  glc reads from L2, past the scalar cache, so no line cached
+// there before the table was last written can be seen.
 __device__ __forceinline__ void scalar_table_entries2(const int32_t* row, int pg, int max_pages,
                                                       int (&out)[2]) {
   const int32_t* p0 = row + min(pg, max_pages - 1);
   const int32_t* p1 = row + min(pg + 1, max_pages - 1);
   int v0, v1;
-  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+  asm volatile("s_load_dword %0, %2, 0x0 glc\n\ts_load_dword %1, %3, 0x0 glc\n\ts_waitcnt lgkmcnt(0)"
                : "=&s"(v0), "=&s"(v1)
                : "s"(p0), "s"(p1)
                : "memory");
@@ -453,7 +454,7 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
     const int page = page_lookup(W, bt_row, a.max_pages, k * kTile / kPage, lane);
     return tile_copy(a, page, ch.len, k, st);
   };
-  // the first tiles' pages through the scalar cache (tiles 0 .. 2 lie in
+  // the first tiles' pages by scalar loads (tiles 0 .. 2 lie in
   // pages pg0 and pg0 + 1), then the page window of the later tiles
   static_assert((3 * kTile) / kPage <= 2, "prologue pages");
   loads();

@@ -142,11 +142,12 @@ __device__ __forceinline__ MLA_LDS uint8_t* stage_base(int st) {
 }
 
 // Entries pg .. pg + 3 of a block-table row (clamped to its max_pages
-// entries) through the scalar cache, waited for in place.  The wait counts
-// scalar loads only: it neither holds on the vector loads in flight nor
-// leaves the compiler a vector load to wait for, whose wait would count
-// every older vector load and copy (so that the prologue's copies would go
-// out one tile at a time).
+// entries) by scalar loads, waited for in place.  The wait counts scalar
+// loads only: it neither holds on the vector loads in flight nor leaves the
+// compiler a vector load to wait for, whose wait would count every older
+// vector load and copy (so that the prologue's copies would go out one tile
+// at a time).  glc reads from L2, past the scalar cache, so no line cached
+// there before the table was last written can be seen.
 __device__ __forceinline__ void scalar_table_entries4(const int32_t* row, int pg, int max_pages,
                                                       int (&out)[4]) {
   const int32_t* p0 = row + min(pg, max_pages - 1);
@@ -155,8 +156,8 @@ __device__ __forceinline__ void scalar_table_entries4(const int32_t* row, int pg
   const int32_t* p3 = row + min(pg + 3, max_pages - 1);
   int v0, v1, v2, v3;
   asm volatile(
-      "s_load_dword %0, %4, 0x0\n\ts_load_dword %1, %5, 0x0\n\t"
-      "s_load_dword %2, %6, 0x0\n\ts_load_dword %3, %7, 0x0\n\ts_waitcnt lgkmcnt(0)"
+      "s_load_dword %0, %4, 0x0 glc\n\ts_load_dword %1, %5, 0x0 glc\n\t"
+      "s_load_dword %2, %6, 0x0 glc\n\ts_load_dword %3, %7, 0x0 glc\n\ts_waitcnt lgkmcnt(0)"
       : "=&s"(v0), "=&s"(v1), "=&s"(v2), "=&s"(v3)
       : "s"(p0), "s"(p1), "s"(p2), "s"(p3)
       : "memory");
