@@ -224,15 +224,20 @@ def test_score_jumps_fp8_cache(late):
     check_against_oracle(wl, got, rows=sample_rows(wl, 10, seed=4))
 
 
-def test_split_count_invariance():
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_split_count_invariance(cfg):
     """One sequence decoded alone and inside a batch of 64 goes through very
     different split plans: alone, its 128 tiles are spread over one chunk per
     tile (128 partials merged by the combine pass); in the batch it gets 4
     chunks of 32 tiles.  The merge is exact up to the bf16 rounding of each
-    partial, so the two outputs agree to bf16 precision, and both match the
-    oracle on sampled heads."""
+    partial (and, for the e4m3 cache, the e4m3 rounding of the probabilities,
+    whose per-tile block scales depend on the chunk's reference), so the two
+    outputs agree to that precision, and both match the oracle on sampled
+    heads.  Alone, the last chunks start in the last page of an exactly sized
+    block-table row, so the decode's reads of the entries after it are
+    clamped to the row."""
     from dataclasses import replace
-    spec = inputs.workload(2)
+    spec = inputs.workload(cfg)
     wl64 = inputs.make_workload(spec)
     wl1 = replace(wl64, spec=replace(spec, batch=1), seqlens=wl64.seqlens[:1].copy(),
                   block_table=wl64.block_table[:1].copy(), q_nope=wl64.q_nope[:1].copy(),
@@ -246,7 +251,7 @@ def test_split_count_invariance():
         a, b = got1[name][0], got64[name][0]
         rel = np.max(np.abs(a - b)) / np.max(np.abs(b))
         print(f"[split] {name}: max |alone - batched| / max |batched| = {rel:.2e}", flush=True)
-        assert rel <= 1e-2, (name, rel)
+        assert rel <= (1e-2 if cfg == 2 else 6e-2), (name, rel)
     lse_diff = np.max(np.abs(got1["lse_latent"][0] - got64["lse_latent"][0]))
     print(f"[split] lse max abs diff {lse_diff:.2e}", flush=True)
-    assert lse_diff <= 1e-3
+    assert lse_diff <= (1e-3 if cfg == 2 else 6e-2)
