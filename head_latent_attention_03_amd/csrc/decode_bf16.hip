@@ -456,7 +456,7 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
   };
   // the first tiles' pages by scalar loads (tiles 0 .. 2 lie in
   // pages pg0 and pg0 + 1), then the page window of the later tiles
-  static_assert((3 * kTile) / kPage <= 2, "prologue pages");
+  static_assert(kPage == 2 * kTile, "tiles 0 .. 2 lie in two pages");
   loads();
   int pgs[2];
   scalar_table_entries2(bt_row, W.pg0, a.max_pages, pgs);

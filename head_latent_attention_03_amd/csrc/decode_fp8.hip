@@ -647,8 +647,9 @@ __device__ __forceinline__ void run_pass(const DecodeArgs& a, State& S, const Ch
                        : __builtin_bit_cast(u16x8, u32x4{kOneBf16 | (kOneBf16 << 16), mneg, 0u, 0u});
   };
 
-  // the prologue's tiles 0 .. AHEAD + 1 lie in pages pg0 .. pg0 + 3
-  static_assert(((AHEAD + 1) * kTile) / kPage + 1 <= 4, "prologue pages");
+  // the prologue's tiles 0 .. AHEAD + 1 lie in pages pg0 .. pg0 + 3 (tile i
+  // of the chunk is at most (i + 1) / 2 pages past its first)
+  static_assert(kPage == 2 * kTile && (AHEAD + 2) / 2 <= 3, "prologue pages");
   if (first) load_query();
   int pgs[4];
   scalar_table_entries4(bt_row, W.pg0, a.max_pages, pgs);
