@@ -456,12 +456,31 @@ def streaming_object(launches, sink_pages=1, window_pages=64):
     return out
 
 
+def plan_split_counts(tiles, row_groups, G):
+    """Chunks per sequence of the decode's split plan (the same rule as the
+    kernels'): proportional counts p = min(t, max(1, floor(G t / NT))) set a
+    chunk budget, B = G when they total at most G and G + U (U units) when
+    not; the chunk length is the shortest C with sum ceil(t / C) <= B, and a
+    sequence of t tiles gets ceil(t / C) chunks."""
+    nt = sum(tiles) * row_groups
+    if nt == 0:
+        return [0] * len(tiles)
+    p = [min(t, max(1, G * t // nt)) if t > 0 else 0 for t in tiles]
+    budget = G if sum(p) * row_groups <= G else G + len(tiles) * row_groups
+    count = lambda c: sum(-(-t // c) for t in tiles) * row_groups
+    lo, hi = -(-nt // budget), max(-(-t // q) for t, q in zip(tiles, p) if q > 0)
+    while lo < hi:
+        mid = (lo + hi) // 2
+        lo, hi = (lo, mid) if count(mid) <= budget else (mid + 1, hi)
+    return [-(-t // hi) for t in tiles]
+
+
 def second_pass_share(wl, cus, limit=108.75):
     """Share of the e4m3 decode's workgroups that must run their chunk twice on
     workload `wl`, from the exact scores (fp32 numpy on the stored values; the
     kernel's e4m3 query moves them slightly): the plan cuts each sequence into
-    chunks of 32-token tiles (s = min(tiles, max(1, floor(G tiles / NT))) chunks
-    per sequence for G compute units).  The kernel works on v_t = s_t +
+    chunks of 32-token tiles (plan_split_counts for G compute units).  The
+    kernel works on v_t = s_t +
     log2(token scale) (log2 units); a row's reference is its largest v in the
     chunk's first tile, and the chunk is redone when any later v of any of its
     rows passes that reference by more than `limit`: 100 for the largest
@@ -476,7 +495,7 @@ def second_pass_share(wl, cus, limit=108.75):
     w_uk = dec(wl.w_uk, "bf16")
     rows_groups = (spec.q_len * spec.n_heads + 127) // 128
     tiles = [(int(L) + 31) // 32 for L in wl.seqlens]
-    nt = sum(tiles) * rows_groups
+    splits = plan_split_counts(tiles, rows_groups, cus)
     redo = chunks = 0
     for b, L in enumerate(wl.seqlens):
         L = int(L)
@@ -501,7 +520,7 @@ def second_pass_share(wl, cus, limit=108.75):
         lim = pos + 1
         sc[np.arange(L)[None, :] >= lim[:, None]] = -np.inf
         n_t = tiles[b]
-        s_u = min(n_t, max(1, (cus * n_t) // nt))
+        s_u = splits[b]
         for c in range(s_u):
             k0, k1 = c * n_t // s_u, (c + 1) * n_t // s_u
             first = sc[:, k0 * 32:min((k0 + 1) * 32, L)].max(axis=1)

@@ -32,18 +32,25 @@ constexpr int kWaves = 4;
 constexpr int kPage = 64;
 
 // ---------------------------------------------------------------------------
-// The split plan, recomputed identically by the decode and combine kernels
-// from the device seqlens (no host round trip).
+// The split plan, computed by every decode workgroup from the device seqlens
+// (no host round trip); the first chunk of each unit records where the
+// combine pass finds the unit's partials.
 //
 // Work unit u = (b, rg): sequence b, row group rg of kRowsPerWG rows of the
 // flattened (query token j, head h) space, rows r = j * n_heads + h.  Unit u
 // has tiles_u = ceil(L_b / kTile) tiles of cached tokens; NT = sum of tiles_u.
-// For a target of G workgroups, unit u is cut into
-//     s_u = min(tiles_u, max(1, floor(G * tiles_u / NT)))
-// chunks of near-equal tile counts (none if tiles_u = 0); chunk c covers tiles
-// [c * tiles_u / s_u, (c + 1) * tiles_u / s_u).  Chunks are numbered in unit
-// order (b-major, rg minor); chunk number = workgroup = partial slot.  At most
-// G + (number of units) chunks exist.
+// Chunks are cut to a length C and a budget B of chunks: with G target
+// workgroups and U units, the proportional counts
+//     p_u = min(tiles_u, max(1, floor(G * tiles_u / NT)))   (0 if tiles_u = 0)
+// decide the budget, B = G when they total at most G (every chunk runs in one
+// wave of workgroups) and B = G + U otherwise (many short units: two waves);
+// then
+//     C = min { c : sum_u ceil(tiles_u / c) <= B },   s_u = ceil(tiles_u / C)
+// chunks of unit u.  The proportional counts meet that bound with
+// c = max_u ceil(tiles_u / p_u), so no chunk is longer than under them.
+// Chunk c of unit u covers tiles [c * tiles_u / s_u, (c + 1) * tiles_u / s_u).
+// Chunks are numbered in unit order (b-major, rg minor); chunk number =
+// workgroup = partial slot.  At most G + U chunks exist.
 __host__ __device__ inline int tiles_of(int len) { return (len + kTile - 1) / kTile; }
 
 __host__ __device__ inline int plan_splits(int tiles_u, int64_t nt, int G) {
@@ -51,6 +58,8 @@ __host__ __device__ inline int plan_splits(int tiles_u, int64_t nt, int G) {
   const int64_t s = (int64_t)G * tiles_u / nt;
   return s < 1 ? 1 : (s > tiles_u ? tiles_u : (int)s);
 }
+
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // Workgroups are dispatched round-robin over the 8 XCDs.  Give consecutive
 // logical ids to workgroups of one XCD so neighbouring chunks (e.g. the chunks
@@ -90,14 +99,64 @@ __device__ __forceinline__ double rope_theta(int i, int d_rope, float base) {
 }
 
 
-// Total tiles NT over all units (every lane gets the same value).
-__device__ inline int64_t plan_total_tiles(const int32_t* seqlens, int batch, int row_groups,
-                                           int lane) {
-  int part = 0;
-  for (int b = lane; b < batch; b += 64) part += tiles_of(seqlens[b]);
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
-  return (int64_t)uni(part) * row_groups;
+// Wave-wide integer reductions and scan on DPP lane moves (VALU; no LDS round
+// trip) and lane reads.  Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadSwap2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowShr1 = 0x111;    // lanes at the start of a row of 16 read 0
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+
+__device__ __forceinline__ int lane_value(int v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+
+__device__ inline int wave_sum_int(int v) {
+  v += dpp_move<kDppQuadSwap1>(v);
+  v += dpp_move<kDppQuadSwap2>(v);
+  v += dpp_move<kDppRowRor4>(v);
+  v += dpp_move<kDppRowRor8>(v);   // every lane: the sum of its row of 16
+  return lane_value(v, 0) + lane_value(v, 16) + lane_value(v, 32) + lane_value(v, 48);
+}
+__device__ inline int wave_max_int(int v) {
+  v = max(v, dpp_move<kDppQuadSwap1>(v));
+  v = max(v, dpp_move<kDppQuadSwap2>(v));
+  v = max(v, dpp_move<kDppRowRor4>(v));
+  v = max(v, dpp_move<kDppRowRor8>(v));
+  return max(max(lane_value(v, 0), lane_value(v, 16)), max(lane_value(v, 32), lane_value(v, 48)));
+}
+// Inclusive prefix sum over the lanes.
+__device__ inline int wave_incl_scan(int v, int lane) {
+  v += dpp_move<kDppRowShr1>(v);
+  v += dpp_move<kDppRowShr2>(v);
+  v += dpp_move<kDppRowShr4>(v);
+  v += dpp_move<kDppRowShr8>(v);   // the scan within each row of 16
+  const int r0 = lane_value(v, 15), r1 = lane_value(v, 31), r2 = lane_value(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// The shortest chunk length c in [ceil(NT / B), longest] whose chunk count
+// count(c) = sum_u ceil(tiles_u / c) is at most B, by bisection (count falls
+// as c grows, and count(longest) <= B holds).
+template <typename Count>
+__device__ inline int plan_cut_search(int64_t nt, int64_t budget, int longest, Count count) {
+  int lo = (int)((nt + budget - 1) / budget), hi = longest;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (count(mid) <= budget)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return hi;
 }
 
 // The chunk number a decode workgroup runs, given the total chunk count C, or
@@ -113,91 +172,127 @@ __device__ inline int plan_chunk_of_block(int block, int C) {
   return g < C ? g : -1;
 }
 
-// Chunks of all units of sequences [0, b_end) (the first chunk number of b_end).
-__device__ inline int plan_chunks_before(const int32_t* seqlens, int b_end, int row_groups,
-                                         int64_t nt, int G, int lane) {
-  int part = 0;
-  for (int b = lane; b < b_end; b += 64)
-    part += plan_splits(tiles_of(seqlens[b]), nt, G) * row_groups;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
-  return uni(part);
-}
-
 struct Chunk {
   int b, rg, c, splits, tiles, len;
 };
 
-// The chunk numbered g; false if g is past the last chunk.
-__device__ inline bool plan_find_chunk(const int32_t* seqlens, int batch, int row_groups,
-                                       int64_t nt, int G, int g, int lane, Chunk& out) {
-  int base = 0;
-  for (int b0 = 0; b0 < batch; b0 += 64) {
-    const int b = b0 + lane;
-    const int cnt = (b < batch) ? plan_splits(tiles_of(seqlens[b]), nt, G) * row_groups : 0;
-    int incl = cnt;
+// Fills `out` for chunk g of sequence b (whose first chunk is `start`).
+__device__ inline void plan_fill_chunk(int b, int len, int cut, int start, int g, Chunk& out) {
+  out.b = uni(b);
+  out.len = uni(len);
+  out.tiles = tiles_of(out.len);
+  out.splits = ceil_div(out.tiles, cut);
+  const int off = g - start;
+  out.rg = off / out.splits;
+  out.c = off % out.splits;
+}
+
+// The plan with the lengths of up to 64 * NB sequences held in registers
+// (sequence 64 i + lane in len[i]): one read of the lengths, then every
+// reduction, the bisection and the search run on registers.
+template <int NB>
+__device__ inline bool plan_locate_regs(const int32_t* seqlens, int batch, int row_groups, int G,
+                                        int block, int lane, int& g, Chunk& out) {
+  int len[NB];
+  int sum = 0;
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const int o = __shfl_up(incl, m, 64);
-      if (lane >= m) incl += o;
-    }
-    const uint64_t hit = __ballot(base + incl > g);
+  for (int i = 0; i < NB; ++i) {
+    const int b = 64 * i + lane;
+    len[i] = b < batch ? seqlens[b] : 0;
+    sum += tiles_of(len[i]);
+  }
+  const int64_t nt = (int64_t)wave_sum_int(sum) * row_groups;
+  if (nt == 0) return false;
+  int ptot = 0, longest = 0;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int t = tiles_of(len[i]);
+    const int p = plan_splits(t, nt, G);
+    ptot += p;
+    longest = max(longest, p > 0 ? ceil_div(t, p) : 0);
+  }
+  const int64_t budget = (int64_t)wave_sum_int(ptot) * row_groups <= G
+                             ? (int64_t)G
+                             : (int64_t)G + (int64_t)batch * row_groups;
+  const int cut = plan_cut_search(nt, budget, wave_max_int(longest), [&](int c) {
+    int part = 0;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) part += ceil_div(tiles_of(len[i]), c);
+    return (int64_t)wave_sum_int(part) * row_groups;
+  });
+  int cnt[NB], incl[NB];
+  int base = 0;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    cnt[i] = ceil_div(tiles_of(len[i]), cut) * row_groups;
+    incl[i] = base + wave_incl_scan(cnt[i], lane);
+    base = lane_value(incl[i], 63);
+  }
+  g = plan_chunk_of_block(block, base);
+  if (g < 0) return false;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const uint64_t hit = __ballot(incl[i] > g);
     if (hit) {
       const int f = uni(__builtin_ctzll(hit));
-      const int start = base + uni(__shfl(incl - cnt, f, 64));
-      out.b = uni(b0 + f);
-      out.len = uni(seqlens[out.b]);
-      out.tiles = tiles_of(out.len);
-      out.splits = plan_splits(out.tiles, nt, G);
-      const int off = g - start;
-      out.rg = off / out.splits;
-      out.c = off % out.splits;
+      plan_fill_chunk(64 * i + f, lane_value(len[i], f), cut,
+                      lane_value(incl[i] - cnt[i], f), g, out);
       return true;
     }
-    base += uni(__shfl(incl, 63, 64));
   }
   return false;
 }
 
-// The chunk a decode workgroup runs (the three functions above in one pass):
-// false if there is none.  Up to 64 sequences, one lane each, the lengths are
-// read once and the total, the chunk count and the search all come from
-// registers; beyond that the general functions run.
+// The same plan for any batch, reading the lengths again for every pass.
+__device__ inline bool plan_locate_mem(const int32_t* seqlens, int batch, int row_groups, int G,
+                                       int block, int lane, int& g, Chunk& out) {
+  int sum = 0;
+  for (int b = lane; b < batch; b += 64) sum += tiles_of(seqlens[b]);
+  const int64_t nt = (int64_t)wave_sum_int(sum) * row_groups;
+  if (nt == 0) return false;
+  int ptot = 0, longest = 0;
+  for (int b = lane; b < batch; b += 64) {
+    const int t = tiles_of(seqlens[b]);
+    const int p = plan_splits(t, nt, G);
+    ptot += p;
+    longest = max(longest, p > 0 ? ceil_div(t, p) : 0);
+  }
+  const int64_t budget = (int64_t)wave_sum_int(ptot) * row_groups <= G
+                             ? (int64_t)G
+                             : (int64_t)G + (int64_t)batch * row_groups;
+  const int cut = plan_cut_search(nt, budget, wave_max_int(longest), [&](int c) {
+    int part = 0;
+    for (int b = lane; b < batch; b += 64) part += ceil_div(tiles_of(seqlens[b]), c);
+    return (int64_t)wave_sum_int(part) * row_groups;
+  });
+  int total = 0;
+  for (int b = lane; b < batch; b += 64) total += ceil_div(tiles_of(seqlens[b]), cut) * row_groups;
+  g = plan_chunk_of_block(block, wave_sum_int(total));
+  if (g < 0) return false;
+  int base = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int b = b0 + lane;
+    const int len = b < batch ? seqlens[b] : 0;
+    const int cnt = ceil_div(tiles_of(len), cut) * row_groups;
+    const int incl = base + wave_incl_scan(cnt, lane);
+    const uint64_t hit = __ballot(incl > g);
+    if (hit) {
+      const int f = uni(__builtin_ctzll(hit));
+      plan_fill_chunk(b0 + f, lane_value(len, f), cut, lane_value(incl - cnt, f), g, out);
+      return true;
+    }
+    base = lane_value(incl, 63);
+  }
+  return false;
+}
+
+// The chunk a decode workgroup runs: false if there is none.
 __device__ inline bool plan_locate(const int32_t* seqlens, int batch, int row_groups, int G,
                                    int block, int lane, int& g, Chunk& out) {
-  if (batch > 64) {
-    const int64_t nt = plan_total_tiles(seqlens, batch, row_groups, lane);
-    if (nt == 0) return false;
-    g = plan_chunk_of_block(block, plan_chunks_before(seqlens, batch, row_groups, nt, G, lane));
-    return g >= 0 && plan_find_chunk(seqlens, batch, row_groups, nt, G, g, lane, out);
-  }
-  const int len = lane < batch ? seqlens[lane] : 0;
-  const int tiles = tiles_of(len);
-  int part = tiles;
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) part += __shfl_xor(part, m, 64);
-  const int64_t nt = (int64_t)uni(part) * row_groups;
-  if (nt == 0) return false;
-  const int splits = plan_splits(tiles, nt, G);
-  const int cnt = splits * row_groups;
-  int incl = cnt;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const int o = __shfl_up(incl, m, 64);
-    if (lane >= m) incl += o;
-  }
-  g = plan_chunk_of_block(block, uni(__shfl(incl, 63, 64)));
-  if (g < 0) return false;
-  const uint64_t hit = __ballot(incl > g);
-  const int f = uni(__builtin_ctzll(hit));
-  out.b = f;
-  out.len = uni(__shfl(len, f, 64));
-  out.tiles = tiles_of(out.len);
-  out.splits = uni(__shfl(splits, f, 64));
-  const int off = g - uni(__shfl(incl - cnt, f, 64));
-  out.rg = off / out.splits;
-  out.c = off % out.splits;
-  return true;
+  if (batch <= 64) return plan_locate_regs<1>(seqlens, batch, row_groups, G, block, lane, g, out);
+  if (batch <= 128) return plan_locate_regs<2>(seqlens, batch, row_groups, G, block, lane, g, out);
+  if (batch <= 256) return plan_locate_regs<4>(seqlens, batch, row_groups, G, block, lane, g, out);
+  return plan_locate_mem(seqlens, batch, row_groups, G, block, lane, g, out);
 }
 
 // 2^x with the hardware v_exp_f32 (results below 2^-126 flush to 0, which

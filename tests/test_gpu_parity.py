@@ -60,12 +60,42 @@ def test_bf16_reduced_ragged(seqlens):
 
 
 def test_bf16_more_sequences_than_a_wave():
-    """70 sequences (the split plan's general path, past one lane per sequence), ragged
-    lengths including an empty one, bf16 and fp8 caches."""
+    """70 sequences (two lengths per lane in the split plan), ragged lengths
+    including an empty one, bf16 and fp8 caches."""
     lens = [int(x) for x in np.random.default_rng(70).integers(0, 160, size=70)]
     lens[5] = 0
     _run_check(inputs.workload(2, batch=70, seqlen=lens))
     _run_check(inputs.workload(4, batch=70, seqlen=lens))
+
+
+@pytest.mark.parametrize("case", ["130_bf16", "300_e4m3", "100_mtp2_one_long"])
+def test_split_plan_large_batches(case):
+    """The split plan at the batch sizes where it changes form: 130 sequences
+    (four lengths per lane), 300 (the plan walks the lengths in memory, e4m3
+    cache), and 100 sequences of two query tokens (200 units) with one 6000-token
+    sequence among short ones, where the proportional chunk counts pass the
+    workgroup target and the chunk budget grows to workgroups + units.  Sampled
+    rows plus 16 heads of each query token of the long sequence."""
+    rng = np.random.default_rng({"130_bf16": 130, "300_e4m3": 300, "100_mtp2_one_long": 100}[case])
+    if case == "130_bf16":
+        spec = inputs.workload(2, batch=130,
+                               seqlen=[int(x) for x in rng.integers(0, 400, size=130)])
+    elif case == "300_e4m3":
+        lens = [int(x) for x in rng.integers(0, 200, size=300)]
+        lens[299] = 0
+        spec = inputs.workload(4, batch=300, seqlen=lens)
+    else:
+        lens = [int(x) for x in rng.integers(1, 100, size=100)]
+        lens[37] = 6000
+        spec = inputs.workload(5, batch=100, seqlen=lens, init="fan_in")
+    wl = inputs.make_workload(spec)
+    rows = sample_rows(wl, 40, seed=5)
+    if case == "100_mtp2_one_long":
+        heads = np.arange(0, spec.n_heads, spec.n_heads // 16)
+        long_rows = np.stack([np.full(32, 37), np.repeat([0, 1], 16), np.tile(heads, 2)], axis=1)
+        rows = np.concatenate([rows, long_rows])
+        rows = rows[np.lexsort((rows[:, 2], rows[:, 1], rows[:, 0]))]
+    _run_check(spec, rows=rows)
 
 
 @pytest.mark.parametrize("n_heads,q_len,seqlens", [(16, 1, [5, 300, 64]),
