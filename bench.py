@@ -159,19 +159,26 @@ def summarize_pmc(fetch_dir, write_dir, kind, workload, copy_mib, commands):
     print(open(path).read())
 
 
-def summarize_trace(db_glob, out_name, title, commands):
+def summarize_trace(db_glob, out_name, title, commands, window=None, bench_log=None):
     """Write a kernel-duration summary (profiles/<out_name>) from a rocprofv3
-    --kernel-trace run: calls, mean, median, min and max per kernel."""
+    --kernel-trace run: calls, mean, median, min and max per kernel.
+    `window` = (kernel name substring, first, end): also the statistics of that
+    kernel's calls first .. end - 1 in start order (e.g. the launches a bench
+    object timed).  `bench_log`: the bench output of the same run, whose
+    roofline timing is copied next to them."""
     import sqlite3
     paths = sorted(glob.glob(db_glob, recursive=True))
     if not paths:
         raise SystemExit(f"no rocprofv3 database matches {db_glob}")
     durs = {}
+    ordered = []
     for path in paths:
         con = sqlite3.connect(path)
         for name, start, end in con.execute("select name, start, end from kernels"):
             durs.setdefault(name, []).append((end - start) / 1e3)
+            ordered.append((start, name, (end - start) / 1e3))
         con.close()
+    ordered.sort()
     out = os.path.join(PROFILES, out_name)
     total = sum(sum(v) for v in durs.values())
     with open(out, "w") as fh:
@@ -185,6 +192,22 @@ def summarize_trace(db_glob, out_name, title, commands):
             short = name.replace("mla::(anonymous namespace)::", "")
             fh.write(f"{short[:72]:72s} {len(v):5d} {v.mean():8.2f} {np.median(v):8.2f} "
                      f"{v.min():8.2f} {v.max():8.2f} {100 * v.sum() / total:5.1f}%\n")
+        if window is not None:
+            sub, first, end = window[0], int(window[1]), int(window[2])
+            calls = [d for _, name, d in ordered if sub in name]
+            v = np.asarray(calls[first:end])
+            if v.size == 0:
+                raise SystemExit(f"no calls {first}..{end - 1} of a kernel matching {sub}")
+            fh.write(f"# calls {first} .. {first + v.size - 1} of the kernel matching '{sub}' "
+                     f"(in start order, of {len(calls)}):\n")
+            fh.write(f"{'  window':72s} {v.size:5d} {v.mean():8.2f} {np.median(v):8.2f} "
+                     f"{v.min():8.2f} {v.max():8.2f}\n")
+        if bench_log is not None:
+            line = [ln for ln in open(bench_log).read().splitlines() if ln.startswith("{")][-1]
+            roof = json.loads(line)["roofline"]
+            fh.write(f"# the bench line of the same run: roofline launch_ms {roof['launch_ms']} "
+                     f"(median {roof['launch_ms_median']}, p10 {roof['launch_ms_p10']}, "
+                     f"p90 {roof['launch_ms_p90']}), frac {roof['frac']}\n")
     print(open(out).read())
 
 
@@ -324,6 +347,12 @@ def calibration_copy(mib):
 
 
 TIME_BATCH = 10   # launches between two timing events
+
+
+def progress(msg):
+    """A line on stderr as each part of the run ends (the JSON result alone goes
+    to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def time_launches(call, launches, warm=30, batch=TIME_BATCH):
@@ -719,6 +748,11 @@ def main():
     ap.add_argument("--summarize-trace", nargs=3, metavar=("DB_GLOB", "OUT_NAME", "TITLE"),
                     help="write profiles/OUT_NAME from rocprofv3 --kernel-trace databases "
                          "(the --pmc-command lines are recorded) and exit")
+    ap.add_argument("--trace-window", nargs=3, metavar=("KERNEL", "FIRST", "END"),
+                    help="with --summarize-trace: also the statistics of calls FIRST .. END-1 "
+                         "of the kernel whose name contains KERNEL")
+    ap.add_argument("--bench-log", help="with --summarize-trace: the bench output of the same "
+                                        "run, whose roofline timing is recorded")
     ap.add_argument("--summarize-counters", nargs=3, metavar=("DB_GLOB", "OUT_NAME", "TITLE"),
                     help="write profiles/OUT_NAME with per-kernel averages of the counters "
                          "in rocprofv3 --pmc databases and exit")
@@ -727,7 +761,7 @@ def main():
         summarize_counters(*args.summarize_counters, args.pmc_command)
         return
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace, args.pmc_command)
+        summarize_trace(*args.summarize_trace, args.pmc_command, args.trace_window, args.bench_log)
         return
     if args.summarize_pmc:
         from head_latent_attention_03_amd import inputs
@@ -786,12 +820,14 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
+    progress(f"{args.steps} steps: {ms_step * 1e3:.1f} us per step")
 
     # the dominant kernel, timed launch by launch in its own loop (HIP events on
     # the launch stream; the events are kept out of the step loop above, whose
     # time they would add to)
     dec_ms = time_decode(db, reps, max(20, args.decode_launches))
     roof = decode_roofline(spec, wl.seqlens, dec_ms, read_traffic(kind_of(spec), spec.name))
+    progress(f"decode roofline: {roof['launch_ms'] * 1e3:.1f} us per launch")
 
     # the cache append of the step's new tokens (the step before decode, timed
     # on its own: it is not part of the metric's step)
@@ -848,7 +884,9 @@ def main():
                                                    torch.cuda.get_device_properties(0).multi_processor_count)
             else:
                 out[name] = decode_object(EXTRA_WORKLOADS[name], args.decode_launches)
+            progress(f"object {name} done")
     if args.cpu_budget > 0:
+        progress(f"cpu baseline: about {args.cpu_budget:.0f} s of the oracle")
         t_cpu, frac, rows_done, threads = cpu_baseline(wl, args.cpu_budget)
         full_s = t_cpu / frac
         model, cores = cpu_info()
