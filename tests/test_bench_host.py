@@ -1,6 +1,7 @@
 """Host logic of bench.py (no GPU): the algorithmic bytes and flops behind
 the roofline figures, the comment-insensitive source hash that keys the HBM
-traffic summaries, and the one-GPU guard.
+traffic summaries, the one-GPU guard, and the host copy of the decode's split
+rule (which sizes the e4m3 second-pass estimate).
 
 The expected byte and flop counts are written out from the shapes here, not
 taken from bench.py: per cached token the cache holds the latent row and the
@@ -67,3 +68,51 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120, cwd=ROOT)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+def test_split_plan_rule():
+    """bench.plan_split_counts, the host copy of the decode's split rule,
+    checked against properties computed here by brute force: the chunk count
+    stays within the budget (G when the proportional counts fit in G, else G
+    plus the units); the chunk length is the shortest that does (every shorter
+    length from 1 up overflows the budget); no chunk is longer than under the
+    proportional counts; every nonempty sequence gets at least one chunk and
+    an empty one none."""
+    rng = np.random.default_rng(5)
+    for trial in range(300):
+        batch = int(rng.integers(1, 90))
+        rg = int(rng.integers(1, 3))
+        G = int(rng.choice([8, 64, 256]))
+        tiles = [int(t) for t in rng.choice([0, 1, 3, 40, 128, int(rng.integers(0, 700))],
+                                            size=batch)]
+        nt = sum(tiles) * rg
+        if nt == 0:
+            continue
+        s = bench.plan_split_counts(tiles, rg, G)
+        prop = [min(t, max(1, G * t // nt)) if t > 0 else 0 for t in tiles]
+        budget = G if sum(prop) * rg <= G else G + batch * rg
+        assert sum(s) * rg <= budget
+        longest = max(_ceil(t, q) for t, q in zip(tiles, s) if q > 0)
+        assert all(q == _ceil(t, longest) for t, q in zip(tiles, s))
+        for c in range(1, longest):
+            assert sum(_ceil(t, c) for t in tiles) * rg > budget, (trial, c)
+        assert longest <= max(_ceil(t, q) for t, q in zip(tiles, prop) if q > 0)
+        assert all((q > 0) == (t > 0) for t, q in zip(tiles, s))
+
+
+def test_split_plan_known_cases():
+    """Uniform B=64 sequences of 128 tiles on 256 CUs: 4 chunks of 32 tiles each.
+    256 units whose proportional counts overflow 256 (short units next to long
+    ones) get the two-wave budget of 256 + 256 chunks."""
+    assert bench.plan_split_counts([128] * 64, 1, 256) == [4] * 64
+    tiles = [2] * 127 + [3000]
+    s = bench.plan_split_counts(tiles, 2, 256)
+    nt = sum(tiles) * 2
+    prop = [min(t, max(1, 256 * t // nt)) for t in tiles]
+    assert sum(prop) * 2 > 256
+    assert 256 < sum(s) * 2 <= 512
+    assert s[:127] == [1] * 127
