@@ -68,15 +68,22 @@ def test_bf16_more_sequences_than_a_wave():
     _run_check(inputs.workload(4, batch=70, seqlen=lens))
 
 
-@pytest.mark.parametrize("case", ["130_bf16", "300_e4m3", "100_mtp2_one_long"])
+SPLIT_CASES = {"130_bf16": 130, "300_e4m3": 300, "100_mtp2_one_long": 100,
+               "140_q2_e4m3": 140, "270_q2_bf16": 270}
+
+
+@pytest.mark.parametrize("case", list(SPLIT_CASES))
 def test_split_plan_large_batches(case):
     """The split plan at the batch sizes where it changes form: 130 sequences
     (four lengths per lane), 300 (the plan walks the lengths in memory, e4m3
     cache), and 100 sequences of two query tokens (200 units) with one 6000-token
     sequence among short ones, where the proportional chunk counts pass the
-    workgroup target and the chunk budget grows to workgroups + units.  Sampled
-    rows plus 16 heads of each query token of the long sequence."""
-    rng = np.random.default_rng({"130_bf16": 130, "300_e4m3": 300, "100_mtp2_one_long": 100}[case])
+    workgroup target and the chunk budget grows to workgroups + units; then the
+    four-per-lane and in-memory forms again with two query tokens (two row
+    groups per sequence: 140 sequences on an e4m3 cache, 270 on bf16), where a
+    unit's chunk number splits into row group and chunk.  Sampled rows plus 16
+    heads of each query token of one sequence."""
+    rng = np.random.default_rng(SPLIT_CASES[case])
     if case == "130_bf16":
         spec = inputs.workload(2, batch=130,
                                seqlen=[int(x) for x in rng.integers(0, 400, size=130)])
@@ -84,13 +91,21 @@ def test_split_plan_large_batches(case):
         lens = [int(x) for x in rng.integers(0, 200, size=300)]
         lens[299] = 0
         spec = inputs.workload(4, batch=300, seqlen=lens)
+    elif case == "140_q2_e4m3":
+        lens = [int(x) for x in rng.integers(0, 300, size=140)]
+        lens[3], lens[37] = 1, 2000
+        spec = inputs.workload(4, batch=140, q_len=2, seqlen=lens)
+    elif case == "270_q2_bf16":
+        lens = [int(x) for x in rng.integers(0, 150, size=270)]
+        lens[0], lens[37] = 0, 1500
+        spec = inputs.workload(5, batch=270, seqlen=lens, init="fan_in")
     else:
         lens = [int(x) for x in rng.integers(1, 100, size=100)]
         lens[37] = 6000
         spec = inputs.workload(5, batch=100, seqlen=lens, init="fan_in")
     wl = inputs.make_workload(spec)
     rows = sample_rows(wl, 40, seed=5)
-    if case == "100_mtp2_one_long":
+    if spec.q_len == 2:
         heads = np.arange(0, spec.n_heads, spec.n_heads // 16)
         long_rows = np.stack([np.full(32, 37), np.repeat([0, 1], 16), np.tile(heads, 2)], axis=1)
         rows = np.concatenate([rows, long_rows])
