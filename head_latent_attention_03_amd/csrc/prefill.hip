@@ -158,11 +158,17 @@ constexpr int V_OFF = R_OFF + KT * R_PITCH;
 constexpr int STAGE = V_OFF + KT * V_PITCH;
 constexpr int KS_N = D_NOPE / 16;        // 8 score k-steps over q^C
 constexpr int KS = KS_N + D_ROPE / 16;   // 12
+constexpr float kLazy = 8.f;             // log2 units a row maximum may pass m by
 
 __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][STAGE];
-  const int b = blockIdx.z, h = blockIdx.y;
-  const int j0 = blockIdx.x * QB;
+  // the row blocks of one (sequence, head) take consecutive logical ids on one
+  // XCD, so that its expanded K and V pass through one L2
+  const int nrb = gridDim.x;
+  const int nblk = nrb * gridDim.y * gridDim.z;
+  const int lid = xcd_logical_id(blockIdx.x + nrb * (blockIdx.y + gridDim.y * blockIdx.z), nblk);
+  const int b = lid / (nrb * gridDim.y), h = (lid / nrb) % gridDim.y;
+  const int j0 = (lid % nrb) * QB;
   const int len = a.seqlens[b];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hh = lane >> 5, lc = lane & 31;
@@ -205,19 +211,24 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
     }
   }
 
-  // tile loads (register staged): K^C and V 4 pieces each, k^R 2 pieces
+  // tile loads, register staged two tiles ahead (two sets, so that a tile's
+  // loads have the compute of two tiles to land in before they are stored
+  // to LDS): K^C and V 4 pieces each, k^R 2 pieces
   const uint8_t* kx = (const uint8_t*)a.kexp + ((int64_t)b * H + h) * a.lpad * 256;
   const uint8_t* vx = (const uint8_t*)a.vexp + ((int64_t)b * H + h) * a.lpad * 256;
   const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
-  u32x4 rk[4], rv[4], rr[2];
-  auto load = [&](int kt) {
+  struct Staged {
+    u32x4 rk[4], rv[4], rr[2];
+  };
+  Staged set0, set1;
+  auto load = [&](int kt, Staged& R) {
     const int t0 = kt * KT;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + 256 * e, row = idx >> 4, pc = idx & 15;
       const int t = min(t0 + row, len - 1);
-      rk[e] = *(const u32x4*)(kx + (int64_t)t * 256 + pc * 16);
-      rv[e] = *(const u32x4*)(vx + (int64_t)t * 256 + pc * 16);
+      R.rk[e] = *(const u32x4*)(kx + (int64_t)t * 256 + pc * 16);
+      R.rv[e] = *(const u32x4*)(vx + (int64_t)t * 256 + pc * 16);
     }
     const int page = bt_row[t0 / kPage];
 #pragma unroll
@@ -225,22 +236,22 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
       const int idx = tid + 256 * e, row = idx >> 3, pc = idx & 7;
       const int t = min(t0 + row, len - 1);
       const int pg = (t / kPage == t0 / kPage) ? page : bt_row[t / kPage];
-      rr[e] = *(const u32x4*)((const uint8_t*)a.kv_rope +
+      R.rr[e] = *(const u32x4*)((const uint8_t*)a.kv_rope +
                               ((int64_t)pg * kPage + (t % kPage)) * (D_ROPE * 2) + pc * 16);
     }
   };
-  auto store = [&](int st) {
+  auto store = [&](int st, const Staged& R) {
     uint8_t* s = s_kv[st];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + 256 * e, row = idx >> 4, pc = idx & 15;
-      *(u32x4*)(s + K_OFF + row * K_PITCH + pc * 16) = rk[e];
-      *(u32x4*)(s + V_OFF + row * V_PITCH + pc * 16) = rv[e];
+      *(u32x4*)(s + K_OFF + row * K_PITCH + pc * 16) = R.rk[e];
+      *(u32x4*)(s + V_OFF + row * V_PITCH + pc * 16) = R.rv[e];
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int idx = tid + 256 * e, row = idx >> 3, pc = idx & 7;
-      *(u32x4*)(s + R_OFF + row * R_PITCH + pc * 16) = rr[e];
+      *(u32x4*)(s + R_OFF + row * R_PITCH + pc * 16) = R.rr[e];
     }
   };
 
@@ -250,32 +261,47 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
   float m = -INFINITY, l = 0.f;
   const bf16x2 one2 = __builtin_bit_cast(bf16x2, 0x3f803f80u);
 
-  if (ntiles > 0) {
-    load(0);
-    store(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < ntiles) load(kt + 1);
+  // one key tile from stage st
+  auto tile_step = [&](int kt, int st) {
     const uint8_t* s = s_kv[st];
     const int t0 = kt * KT;
-    // scores of the two 32-key blocks
-    f32x16 sc[2];
+    // scores of the two 32-key blocks: every K operand is read into its own
+    // registers first, then the two blocks' MFMA chains alternate (a read
+    // waited for right before its MFMA would cost the MFMA an LDS round trip)
+    u16x8 kv[2][KS];
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk) {
-      sc[bk] = f32x16{};
-      const int key = 32 * bk + lc;
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        u16x8 kv;
-        if (ks < KS_N)
-          kv = *(const u16x8*)(s + K_OFF + key * K_PITCH + (ks * 16 + hh * 8) * 2);
-        else
-          kv = *(const u16x8*)(s + R_OFF + key * R_PITCH + ((ks - KS_N) * 16 + hh * 8) * 2);
-        sc[bk] = mfma32(kv, q[ks], sc[bk]);
+      for (int bk = 0; bk < 2; ++bk) {
+        const int key = 32 * bk + lc;
+        kv[bk][ks] = ks < KS_N
+                         ? *(const u16x8*)(s + K_OFF + key * K_PITCH + (ks * 16 + hh * 8) * 2)
+                         : *(const u16x8*)(s + R_OFF + key * R_PITCH +
+                                           ((ks - KS_N) * 16 + hh * 8) * 2);
       }
-    }
+    f32x16 sc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk) sc[bk] = mfma32(kv[bk][ks], q[ks], sc[bk]);
+    // the V^T operands of the output product, read now so that they land
+    // while the softmax runs: k-step (bk, kb) covers keys
+    // 32bk + 16kb + {4hh + r, 8 + 4hh + r}
+    const int g1 = (lane >> 4) & 1, r = (lane & 15) >> 2, qd = lane & 3;
+    u16x8 va[2][2][D_V / 32];
+#pragma unroll
+    for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = 32 * bk + 16 * kb + 4 * hh + r;
+#pragma unroll
+        for (int db = 0; db < D_V / 32; ++db) {
+          const uint8_t* p = s + V_OFF + key * V_PITCH + (32 * db + 16 * g1 + 4 * qd) * 2;
+          const u16x4 lo4 = lds_read_tr16((const MLA_LDS uint8_t*)(p));
+          const u16x4 hi4 = lds_read_tr16((const MLA_LDS uint8_t*)(p + 8 * V_PITCH));
+          va[bk][kb][db] = u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+        }
+      }
     // online softmax (log2 units); lane: row lc, keys 32bk + 8(i >> 2) + 4hh + (i & 3)
     float x[2][16];
     float mt = -INFINITY;
@@ -288,9 +314,14 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
         mt = fmaxf(mt, x[bk][i]);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);
-    if (mn > m) {
-      // a row whose maximum grew rescales its output (m = -inf: nothing yet)
+    // Lazy rescaling: a row's reference m moves only when the tile's maximum
+    // passes it by more than kLazy log2 units, so probabilities up to 2^kLazy
+    // stay in P (fine in bf16 and in the fp32 sums) and most tiles skip the
+    // output rescale; the wave takes it when any of its rows needs it.  A row
+    // with no visible key yet keeps m = -inf and P = 0.
+    const bool grow = mt > m + kLazy;
+    if (__ballot(grow)) {
+      const float mn = grow ? mt : m;
       const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mn);
       l *= alpha;
 #pragma unroll
@@ -315,28 +346,33 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
         pk[bk][kb] = __builtin_bit_cast(u16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
       }
     l += psum;
-    // O^T += V^T P^T: k-step (bk, kb) covers keys 32bk + 16kb + {4hh + r, 8 + 4hh + r}
-    const int g1 = (lane >> 4) & 1, r = (lane & 15) >> 2, qd = lane & 3;
+    // O^T += V^T P^T
 #pragma unroll
     for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key = 32 * bk + 16 * kb + 4 * hh + r;
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < D_V / 32; ++db) {
-          const uint8_t* p = s + V_OFF + key * V_PITCH + (32 * db + 16 * g1 + 4 * qd) * 2;
-          const u16x4 lo4 = lds_read_tr16((const MLA_LDS uint8_t*)(p));
-          const u16x4 hi4 = lds_read_tr16((const MLA_LDS uint8_t*)(p + 8 * V_PITCH));
-          const u16x8 va = u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-          o[db] = mfma32(va, pk[bk][kb], o[db]);
-        }
-      }
-    // (stage st ^ 1 was last read in the previous iteration, which every
-    // wave left at the barrier below)
-    if (kt + 1 < ntiles) {
-      store(st ^ 1);
-      __syncthreads();
-    }
+        for (int db = 0; db < D_V / 32; ++db) o[db] = mfma32(va[bk][kb][db], pk[bk][kb], o[db]);
+  };
+  // Tile kt sits in stage kt & 1 and is read while the loads of tile kt + 2
+  // are in flight; then tile kt + 1 (loaded during the previous tile) is
+  // stored to the other stage, whose tile kt - 1 every wave left at the last
+  // barrier, and the barrier publishes it.
+  if (ntiles > 0) load(0, set0);
+  if (ntiles > 1) load(1, set1);
+  if (ntiles > 0) store(0, set0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    if (kt + 2 < ntiles) load(kt + 2, set0);
+    tile_step(kt, 0);
+    if (kt + 1 >= ntiles) break;
+    store(1, set1);
+    __syncthreads();
+    if (kt + 3 < ntiles) load(kt + 3, set1);
+    tile_step(kt + 1, 1);
+    if (kt + 2 >= ntiles) break;
+    store(0, set0);
+    __syncthreads();
   }
   // normalise and store: lane holds row lc, dims 32db + 8(i >> 2) + 4hh + (i & 3)
   const float lsum = l + __shfl_xor(l, 32, 64);
