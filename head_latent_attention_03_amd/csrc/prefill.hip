@@ -302,18 +302,31 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
           va[bk][kb][db] = u16x8{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
         }
       }
-    // online softmax (log2 units); lane: row lc, keys 32bk + 8(i >> 2) + 4hh + (i & 3)
+    // online softmax (log2 units); lane: row lc, keys 32bk + 8(i >> 2) + 4hh + (i & 3).
+    // x holds the raw scores (keys past a row's limit: -inf, applied only on
+    // tiles that some row of the wave does not see whole); the scale
+    // (positive) goes into the maximum here and into the exponent's FMA below
     float x[2][16];
     float mt = -INFINITY;
+    if (__ballot(t0 + KT > lim) == 0) {
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
+      for (int bk = 0; bk < 2; ++bk)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = t0 + 32 * bk + 8 * (i >> 2) + 4 * hh + (i & 3);
-        x[bk][i] = t < lim ? sc[bk][i] * a.scale_log2 : -INFINITY;
-        mt = fmaxf(mt, x[bk][i]);
-      }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        for (int i = 0; i < 16; ++i) {
+          x[bk][i] = sc[bk][i];
+          mt = fmaxf(mt, x[bk][i]);
+        }
+    } else {
+#pragma unroll
+      for (int bk = 0; bk < 2; ++bk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int t = t0 + 32 * bk + 8 * (i >> 2) + 4 * hh + (i & 3);
+          x[bk][i] = t < lim ? sc[bk][i] : -INFINITY;
+          mt = fmaxf(mt, x[bk][i]);
+        }
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * a.scale_log2;
     // Lazy rescaling: a row's reference m moves only when the tile's maximum
     // passes it by more than kLazy log2 units, so probabilities up to 2^kLazy
     // stay in P (fine in bf16 and in the fp32 sums) and most tiles skip the
@@ -339,7 +352,8 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int i = 8 * kb + 2 * c;
-          w4[c] = pack_bf16x2(fast_exp2(x[bk][i] - msub), fast_exp2(x[bk][i + 1] - msub));
+          w4[c] = pack_bf16x2(fast_exp2(fmaf(x[bk][i], a.scale_log2, -msub)),
+                              fast_exp2(fmaf(x[bk][i + 1], a.scale_log2, -msub)));
           psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w4[c]), one2, psum,
                                                  false);
         }
