@@ -47,102 +47,159 @@ constexpr int D_V = 128;
 constexpr int D_ROPE = 64;
 
 // ---------------------------------------------------------------------------
-// expansion GEMM: workgroup = (128 tokens of sequence b, 128 output columns =
-// one half (K^C or V) of one head); wave w computes rows 64 (w >> 1) .. +63
-// and columns 64 (w & 1) .. +63 as 2 x 2 blocks of 32 x 32
-constexpr int EX_M = 128, EX_N = 128, EX_K = 64;   // tile and k-chunk
-constexpr int EX_PITCH = EX_K * 2 + 16;            // LDS bytes per row (16 B pad)
-constexpr int EX_TILE = EX_M * EX_PITCH;
+// expansion GEMM: workgroup = (head h, half p: K^C or V, sequence b, slice of
+// its tokens).  Wave w keeps rows n = 32w .. 32w+31 of W_UK[h] (p = 0) or
+// W_UV[h] (p = 1), all 512 k, in 128 registers as the A operand of
+// D^T = W c^T, and the latent streams past them through a ring of EX_NS
+// stages of 32 tokens, copied straight from HBM into LDS EX_AHEAD tiles
+// ahead.  Two workgroups share a CU, so one's MFMAs run while the other waits.
+// Chunk c of token row r's 1 KiB sits at slot c ^ (r & 15) of the row, so
+// that the 16 lanes of a 16-byte read (rows r .. r + 15, one chunk) fall on 16
+// different bank groups.  A 32-token tile lies inside one 64-token page (its
+// rows past the sequence end re-read the last token, which lies in the same
+// page); the slice's pages are read into LDS first, so that no vector load
+// the compiler waits for sits among the copies.
+constexpr int EX_T = 32;                       // tokens per tile
+constexpr int EX_NS = 2;                       // ring stages
+constexpr int EX_AHEAD = EX_NS - 1;            // tiles whose copies are in flight
+constexpr int EX_OCC = 2;                      // workgroups per CU (64 KiB of LDS, 238 registers each)
+constexpr int EX_ROW = D_LAT * 2;              // 1 KiB latent row
+constexpr int EX_STAGE = EX_T * EX_ROW;        // 32 KiB
+constexpr int EX_KS = D_LAT / 16;              // 32 MFMA k-steps
+constexpr int EX_MAX_SLICE = 128;              // tiles per slice at most (4096 tokens)
+constexpr int EX_RB = 4;                       // latent operand reads issued a group ahead
 
-__global__ __launch_bounds__(256, 2) void expand_kv_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][EX_TILE];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][EX_TILE];
-  const int b = blockIdx.z;
+template <int N>
+__device__ __forceinline__ void ex_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// wait until at most `later` tiles' copies (EX_T / 4 per wave each) are
+// outstanding (later < EX_AHEAD)
+template <int L = 0>
+__device__ __forceinline__ void ex_wait_tiles(int later) {
+  if constexpr (L < EX_AHEAD - 1) {
+    if (later <= L) {
+      ex_wait_vm<L * (EX_T / 4)>();
+      return;
+    }
+    ex_wait_tiles<L + 1>(later);
+  } else {
+    ex_wait_vm<L * (EX_T / 4)>();
+  }
+}
+
+__device__ __forceinline__ void ex_copy16(const void* sbase, uint32_t voff,
+                                          const MLA_LDS uint8_t* lds_base) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(m0), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+__global__ __launch_bounds__(256, EX_OCC) void expand_kv_kernel(PrefillArgs a, int slice_tiles) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_lat[EX_NS][EX_STAGE];
+  __shared__ int32_t s_page[EX_MAX_SLICE / 2 + 1];
+  const int h = blockIdx.x >> 1, part = blockIdx.x & 1, b = blockIdx.y;
   const int len = a.seqlens[b];
-  const int t0 = blockIdx.x * EX_M;
-  if (t0 >= len) return;
-  const int h = blockIdx.y >> 1, part = blockIdx.y & 1;   // part 0: K^C, 1: V
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tile0 = blockIdx.z * slice_tiles;
+  const int ntiles = min((len + EX_T - 1) / EX_T - tile0, slice_tiles);
+  if (ntiles <= 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, lc = lane & 31;
   const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
-  const uint8_t* lat = (const uint8_t*)a.kv_lat;
-  const uint8_t* wmat = (const uint8_t*)(part ? a.w_uv : a.w_uk) + (int64_t)h * 128 * D_LAT * 2;
-
-  // this thread's 4 latent chunks and 4 weight chunks of each k-chunk:
-  // row = idx >> 3, 16-byte piece = idx & 7, idx = tid + 256 e
-  const uint8_t* arow[4];
-  const uint8_t* brow[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int idx = tid + 256 * e, row = idx >> 3, pc = idx & 7;
-    const int t = min(t0 + row, len - 1);     // rows past the end: any valid row
-    const int page = bt_row[t / kPage];
-    arow[e] = lat + ((int64_t)page * kPage + (t % kPage)) * (D_LAT * 2) + pc * 16;
-    brow[e] = wmat + (int64_t)row * (D_LAT * 2) + pc * 16;
-  }
-  u32x4 ra[4], rb[4];
-  auto load = [&](int kc) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      ra[e] = *(const u32x4*)(arow[e] + kc * EX_K * 2);
-      rb[e] = *(const u32x4*)(brow[e] + kc * EX_K * 2);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int idx = tid + 256 * e, row = idx >> 3, pc = idx & 7;
-      *(u32x4*)(&s_a[buf][row * EX_PITCH + pc * 16]) = ra[e];
-      *(u32x4*)(&s_b[buf][row * EX_PITCH + pc * 16]) = rb[e];
-    }
-  };
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-  const int mrow = 64 * (w >> 1), ncol = 64 * (w & 1);
-  load(0);
-  store(0);
+  // pages of tiles tile0 .. tile0 + ntiles - 1 (two tiles per page; a slice
+  // may start in the middle of a page)
+  const int pg0 = tile0 * EX_T / kPage;
+  const int npg = (tile0 + ntiles - 1) * EX_T / kPage - pg0 + 1;
+  if (tid < npg) s_page[tid] = bt_row[pg0 + tid];
   __syncthreads();
-  constexpr int NKC = D_LAT / EX_K;
-  for (int kc = 0; kc < NKC; ++kc) {
-    const int buf = kc & 1;
-    if (kc + 1 < NKC) load(kc + 1);
+
+  // tile kt's rows 8w .. 8w + 7 into stage st: lane l brings chunk l ^ (r & 15)
+  // of row r (rows past the sequence re-read its last token, finite data whose
+  // outputs are not stored)
+  const uint8_t* lat = (const uint8_t*)a.kv_lat;
+  // row r = 8w + j: r & 15 = 8 (w & 1) + j
+  const uint32_t lane_key = (uint32_t)(lane ^ (8 * (w & 1)));
+  auto copy_tile = [&](int kt, int st) {
+    const uint8_t* pbase =
+        lat + (int64_t)__builtin_amdgcn_readfirstlane(s_page[(tile0 + kt) * EX_T / kPage - pg0]) *
+                  kPage * EX_ROW;
 #pragma unroll
-    for (int ks = 0; ks < EX_K / 16; ++ks) {
-      u16x8 av[2], bv[2];
+    for (int j = 0; j < EX_T / 4; ++j) {
+      const int r = (EX_T / 4) * w + j;
+      const int t = min((tile0 + kt) * EX_T + r, len - 1);
+      ex_copy16(pbase + (int64_t)(t % kPage) * EX_ROW, (lane_key ^ (uint32_t)j) << 4,
+                (MLA_LDS uint8_t*)s_lat[st] + r * EX_ROW);
+    }
+  };
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        av[i] = *(const u16x8*)(&s_a[buf][(mrow + 32 * i + lc) * EX_PITCH + (ks * 16 + 8 * hh) * 2]);
-        bv[i] = *(const u16x8*)(&s_b[buf][(ncol + 32 * i + lc) * EX_PITCH + (ks * 16 + 8 * hh) * 2]);
+  for (int kt = 0; kt < EX_AHEAD; ++kt)
+    if (kt < ntiles) copy_tile(kt, kt);
+
+  // A operands: W rows n = 32w + lc, k = 16 ks + 8 hh .. + 7
+  u16x8 wr[EX_KS];
+  {
+    const uint16_t* pw = (const uint16_t*)(part ? a.w_uv : a.w_uk) +
+                         ((int64_t)h * 128 + 32 * w + lc) * D_LAT + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < EX_KS; ++ks) wr[ks] = *(const u16x8*)(pw + 16 * ks);
+  }
+  // the compiler's wait for W (all older copies with it) happens here, once
+#pragma unroll
+  for (int ks = 0; ks < EX_KS; ++ks) asm volatile("" ::"v"(wr[ks]));
+
+  uint16_t* dst = (uint16_t*)(part ? a.vexp : a.kexp) + ((int64_t)b * a.n_heads + h) * a.lpad * 128;
+  for (int kt = 0; kt < ntiles; ++kt) {
+    // tile kt's copies have landed (those of up to EX_AHEAD - 1 later tiles
+    // may not)
+    ex_wait_tiles(min(EX_AHEAD - 1, ntiles - 1 - kt));
+    __syncthreads();
+    // stage (kt + EX_AHEAD) % EX_NS held tile kt - 1, which every wave left
+    // before the barrier
+    if (kt + EX_AHEAD < ntiles) copy_tile(kt + EX_AHEAD, (kt + EX_AHEAD) % EX_NS);
+    const MLA_LDS uint8_t* st = (const MLA_LDS uint8_t*)s_lat[kt % EX_NS] + lc * EX_ROW;
+    // two accumulators (even and odd k-steps) so that consecutive MFMAs do not
+    // wait on each other
+    // The latent operands of k-steps k0 + EX_RB .. are read before the MFMAs of
+    // k0 .. (scheduling barriers keep that order), so every read has EX_RB
+    // MFMAs to land behind.
+    f32x16 d0 = f32x16{}, d1 = f32x16{};
+    auto read_group = [&](int k0, u16x8(&cb)[EX_RB]) {
+#pragma unroll
+      for (int e = 0; e < EX_RB; ++e) {
+        const int c = 2 * (k0 + e) + hh;
+        cb[e] = *(const MLA_LDS u16x8*)(st + ((c ^ (lc & 15)) << 4));
+      }
+    };
+    u16x8 cur[EX_RB], nxt[EX_RB];
+    read_group(0, cur);
+#pragma unroll
+    for (int k0 = 0; k0 < EX_KS; k0 += EX_RB) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (k0 + EX_RB < EX_KS) read_group(k0 + EX_RB, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int e = 0; e < EX_RB; e += 2) {
+        d0 = mfma32(wr[k0 + e], cur[e], d0);
+        d1 = mfma32(wr[k0 + e + 1], cur[e + 1], d1);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(av[i], bv[j], acc[i][j]);
+      for (int e = 0; e < EX_RB; ++e) cur[e] = nxt[e];
     }
-    if (kc + 1 < NKC) {
-      store(buf ^ 1);
-      __syncthreads();
+    // lane: token lc of the tile, dims 32w + 8g + 4hh .. + 3 (g = 0..3)
+    const int t = (tile0 + kt) * EX_T + lc;
+    if (t < len) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t o = (int64_t)t * 128 + 32 * w + 8 * g + 4 * hh;
+        *(u32x2*)(dst + o) =
+            u32x2{pack_bf16x2(d0[4 * g] + d1[4 * g], d0[4 * g + 1] + d1[4 * g + 1]),
+                  pack_bf16x2(d0[4 * g + 2] + d1[4 * g + 2], d0[4 * g + 3] + d1[4 * g + 3])};
+      }
     }
   }
-  // lane holds rows 8(r >> 2) + 4hh + (r & 3) of each 32-row block, column lc
-  uint16_t* dst = (uint16_t*)(part ? a.vexp : a.kexp) + ((int64_t)b * a.n_heads + h) * a.lpad * 128;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = t0 + mrow + 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (t < len) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float v = acc[i][j][r];
-          dst[(int64_t)t * 128 + ncol + 32 * j + lc] =
-              (uint16_t)(__builtin_bit_cast(uint32_t, pack_bf16x2(v, 0.f)) & 0xffffu);
-        }
-      }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -407,9 +464,15 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  const int tok_blocks = (a.lpad + EX_M - 1) / EX_M;
-  hipLaunchKernelGGL(expand_kv_kernel, dim3(tok_blocks, 2 * a.n_heads, a.batch), dim3(256), 0, s,
-                     a);
+  // slices of at most EX_MAX_SLICE tiles, enough of them for about 512 workgroups
+  const int max_tiles = (a.lpad + EX_T - 1) / EX_T;
+  const int want = (512 + 2 * a.n_heads * a.batch - 1) / (2 * a.n_heads * a.batch);
+  int slices = max((max_tiles + EX_MAX_SLICE - 1) / EX_MAX_SLICE, min(want, max_tiles));
+  if (slices < 1) slices = 1;
+  const int slice_tiles = (max_tiles + slices - 1) / slices;
+  slices = (max_tiles + slice_tiles - 1) / slice_tiles;
+  hipLaunchKernelGGL(expand_kv_kernel, dim3(2 * a.n_heads, a.batch, slices), dim3(256), 0, s, a,
+                     slice_tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attn_kernel, dim3((a.q_len + QB - 1) / QB, a.n_heads, a.batch), dim3(256), 0,
