@@ -28,6 +28,8 @@
 // from LDS, Q^T from registers), so each lane holds one query row and 16
 // keys per 32-key block; O^T += V^T P^T with P^T straight from the score
 // registers and V^T read with the LDS transpose read in the same key order.
+// Key tiles of 32 keep a workgroup small enough (registers and LDS) for two
+// to share a CU.
 #include "mla_common.hpp"
 #include "mla_internal.hpp"
 
@@ -205,7 +207,11 @@ __global__ __launch_bounds__(256, EX_OCC) void expand_kv_kernel(PrefillArgs a, i
 // ---------------------------------------------------------------------------
 // attention: workgroup = (128 query rows of sequence b, head h)
 constexpr int QB = 128;                  // query rows per workgroup
-constexpr int KT = 64;                   // keys per tile (one cache page)
+constexpr int KT = 32;                   // keys per tile (half a cache page)
+constexpr int NBK = KT / 32;             // 32-key MFMA blocks per tile
+constexpr int NPK = KT * 16 / 256;       // 16-byte K^C (and V) pieces per thread and tile
+constexpr int NPR = KT * 8 / 256;        // 16-byte rotary pieces per thread and tile
+constexpr int ATT_OCC = 2;               // workgroups per CU (247 registers, 2 x 23.5 KiB of LDS each)
 constexpr int K_PITCH = D_NOPE * 2 + 16; // 272: conflict-free 16-byte row reads
 constexpr int R_PITCH = D_ROPE * 2 + 16; // 144
 constexpr int V_PITCH = D_V * 2 + 64;    // 320: conflict-free transpose reads
@@ -217,7 +223,7 @@ constexpr int KS_N = D_NOPE / 16;        // 8 score k-steps over q^C
 constexpr int KS = KS_N + D_ROPE / 16;   // 12
 constexpr float kLazy = 8.f;             // log2 units a row maximum may pass m by
 
-__global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, ATT_OCC) void attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][STAGE];
   // the row blocks of one (sequence, head) take consecutive logical ids on one
   // XCD, so that its expanded K and V pass through one L2
@@ -275,13 +281,13 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
   const uint8_t* vx = (const uint8_t*)a.vexp + ((int64_t)b * H + h) * a.lpad * 256;
   const int32_t* bt_row = a.block_table + (int64_t)b * a.max_pages;
   struct Staged {
-    u32x4 rk[4], rv[4], rr[2];
+    u32x4 rk[NPK], rv[NPK], rr[NPR];
   };
   Staged set0, set1;
   auto load = [&](int kt, Staged& R) {
     const int t0 = kt * KT;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < NPK; ++e) {
       const int idx = tid + 256 * e, row = idx >> 4, pc = idx & 15;
       const int t = min(t0 + row, len - 1);
       R.rk[e] = *(const u32x4*)(kx + (int64_t)t * 256 + pc * 16);
@@ -289,7 +295,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
     }
     const int page = bt_row[t0 / kPage];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < NPR; ++e) {
       const int idx = tid + 256 * e, row = idx >> 3, pc = idx & 7;
       const int t = min(t0 + row, len - 1);
       const int pg = (t / kPage == t0 / kPage) ? page : bt_row[t / kPage];
@@ -300,13 +306,13 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
   auto store = [&](int st, const Staged& R) {
     uint8_t* s = s_kv[st];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < NPK; ++e) {
       const int idx = tid + 256 * e, row = idx >> 4, pc = idx & 15;
       *(u32x4*)(s + K_OFF + row * K_PITCH + pc * 16) = R.rk[e];
       *(u32x4*)(s + V_OFF + row * V_PITCH + pc * 16) = R.rv[e];
     }
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < NPR; ++e) {
       const int idx = tid + 256 * e, row = idx >> 3, pc = idx & 7;
       *(u32x4*)(s + R_OFF + row * R_PITCH + pc * 16) = R.rr[e];
     }
@@ -325,29 +331,31 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
     // scores of the two 32-key blocks: every K operand is read into its own
     // registers first, then the two blocks' MFMA chains alternate (a read
     // waited for right before its MFMA would cost the MFMA an LDS round trip)
-    u16x8 kv[2][KS];
+    u16x8 kv[NBK][KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk) {
+      for (int bk = 0; bk < NBK; ++bk) {
         const int key = 32 * bk + lc;
         kv[bk][ks] = ks < KS_N
                          ? *(const u16x8*)(s + K_OFF + key * K_PITCH + (ks * 16 + hh * 8) * 2)
                          : *(const u16x8*)(s + R_OFF + key * R_PITCH +
                                            ((ks - KS_N) * 16 + hh * 8) * 2);
       }
-    f32x16 sc[2] = {f32x16{}, f32x16{}};
+    f32x16 sc[NBK];
+#pragma unroll
+    for (int bk = 0; bk < NBK; ++bk) sc[bk] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk) sc[bk] = mfma32(kv[bk][ks], q[ks], sc[bk]);
+      for (int bk = 0; bk < NBK; ++bk) sc[bk] = mfma32(kv[bk][ks], q[ks], sc[bk]);
     // the V^T operands of the output product, read now so that they land
     // while the softmax runs: k-step (bk, kb) covers keys
     // 32bk + 16kb + {4hh + r, 8 + 4hh + r}
     const int g1 = (lane >> 4) & 1, r = (lane & 15) >> 2, qd = lane & 3;
-    u16x8 va[2][2][D_V / 32];
+    u16x8 va[NBK][2][D_V / 32];
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
+    for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int key = 32 * bk + 16 * kb + 4 * hh + r;
@@ -363,11 +371,11 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
     // x holds the raw scores (keys past a row's limit: -inf, applied only on
     // tiles that some row of the wave does not see whole); the scale
     // (positive) goes into the maximum here and into the exponent's FMA below
-    float x[2][16];
+    float x[NBK][16];
     float mt = -INFINITY;
     if (__ballot(t0 + KT > lim) == 0) {
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk)
+      for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           x[bk][i] = sc[bk][i];
@@ -375,7 +383,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
         }
     } else {
 #pragma unroll
-      for (int bk = 0; bk < 2; ++bk)
+      for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int t = t0 + 32 * bk + 8 * (i >> 2) + 4 * hh + (i & 3);
@@ -399,10 +407,10 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
       m = mn;
     }
     const float msub = m == -INFINITY ? 0.f : m;
-    u16x8 pk[2][2];
+    u16x8 pk[NBK][2];
     float psum = 0.f;
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
+    for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         uint32_t w4[4];
@@ -419,7 +427,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(PrefillArgs a) {
     l += psum;
     // O^T += V^T P^T
 #pragma unroll
-    for (int bk = 0; bk < 2; ++bk)
+    for (int bk = 0; bk < NBK; ++bk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
