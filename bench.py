@@ -355,6 +355,28 @@ def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# The GPU's clock comes up only after about half a second of continuous work
+# (measured: B=64 L=4096 bf16 decode at 113.7 us per launch after 2 s idle,
+# 77.7 us after 0.5 s of back-to-back decodes, 78.1 us after 3.5 s), so every
+# timed loop first runs its work untimed for at least this long.
+CLOCK_WARM_S = 0.5
+
+
+def warm_clock(call, seconds=CLOCK_WARM_S):
+    """Run `call(i)` back to back, untimed, for at least `seconds` of wall time
+    (synchronising every few calls); returns the number of calls."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(8):
+            call(n)
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
 def time_launches(call, launches, warm=30, batch=TIME_BATCH):
     """Per-launch durations (ms) of back-to-back calls of `call(i)` (the i-th
     launch).  HIP events on the launch stream bracket each batch of `batch`
@@ -362,10 +384,12 @@ def time_launches(call, launches, warm=30, batch=TIME_BATCH):
     a timing event between every two launches adds 4-7 us to each (measured:
     80.0 us per B=64 L=4096 bf16 decode back to back, 84-85 us with an event
     pair around each).  The batches follow one another without a host
-    synchronisation, after `warm` launches that bring the clocks up.  Returns
-    one mean per batch, ceil(launches / batch) batches."""
+    synchronisation, after at least `warm` launches and CLOCK_WARM_S seconds
+    of untimed launches that bring the clock up.  Returns one mean per batch,
+    ceil(launches / batch) batches."""
     import torch
     stream = torch.cuda.current_stream()
+    warm_clock(call)
     for i in range(warm):
         call(i)
     nb = max(1, -(-launches // batch))
@@ -811,6 +835,8 @@ def main():
         db.decode(kv_latent=lat, kv_scale=sc, kv_rope=rope)
         db.combine(with_uv=True)
 
+    # the clock's own warm-up, then the W counted warm-up steps (all untimed)
+    warm_steps = warm_clock(step)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -844,6 +870,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_warmup": {"seconds": CLOCK_WARM_S, "steps": warm_steps,
+                         "note": "untimed steps run before the W warm-up steps, until the GPU "
+                                 "clock has had half a second of continuous work"},
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
