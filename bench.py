@@ -195,10 +195,13 @@ def summarize_trace(db_glob, out_name, title, commands, window=None, bench_log=N
         if window is not None:
             sub, first, end = window[0], int(window[1]), int(window[2])
             calls = [d for _, name, d in ordered if sub in name]
-            v = np.asarray(calls[first:end])
+            # (negative indices count from the end; END 0 is the end)
+            sel = calls[first:(end if end != 0 else None)]
+            v = np.asarray(sel)
             if v.size == 0:
                 raise SystemExit(f"no calls {first}..{end - 1} of a kernel matching {sub}")
-            fh.write(f"# calls {first} .. {first + v.size - 1} of the kernel matching '{sub}' "
+            lo = first if first >= 0 else len(calls) + first
+            fh.write(f"# calls {lo} .. {lo + v.size - 1} of the kernel matching '{sub}' "
                      f"(in start order, of {len(calls)}):\n")
             fh.write(f"{'  window':72s} {v.size:5d} {v.mean():8.2f} {np.median(v):8.2f} "
                      f"{v.min():8.2f} {v.max():8.2f}\n")
@@ -362,6 +365,9 @@ def progress(msg):
 CLOCK_WARM_S = 0.5
 
 
+_untimed = {"last": 0}   # untimed launches before the last time_launches batch
+
+
 def warm_clock(call, seconds=CLOCK_WARM_S):
     """Run `call(i)` back to back, untimed, for at least `seconds` of wall time
     (synchronising every few calls); returns the number of calls."""
@@ -389,7 +395,7 @@ def time_launches(call, launches, warm=30, batch=TIME_BATCH):
     ceil(launches / batch) batches."""
     import torch
     stream = torch.cuda.current_stream()
-    warm_clock(call)
+    _untimed["last"] = warm_clock(call) + warm
     for i in range(warm):
         call(i)
     nb = max(1, -(-launches // batch))
@@ -438,6 +444,7 @@ def decode_roofline(spec, seqlens, ms, traffic):
         "launch_ms_p10": round(float(np.percentile(ms, 10)), 5),
         "launch_ms_p90": round(float(np.percentile(ms, 90)), 5),
         "timed_launches": int(len(ms)) * TIME_BATCH,
+        "untimed_launches": _untimed["last"],
         "timing": f"HIP events around each batch of {TIME_BATCH} back-to-back launches; "
                   "launch_ms is the mean, median/p10/p90 are over the batch means",
         "algorithmic_bytes": int(dec_b), "algorithmic_flops": int(dec_f),
