@@ -184,7 +184,8 @@ __device__ __forceinline__ void issue_tile(const TileCopy& c, int w, int lane) {
   for (int j = 0; j < kDma; ++j) issue_part(c, j, w, lane);
 }
 
-// The copies of a tile wholly inside the sequence, with no per-copy address
+// The copies of a tile wholly inside the sequence (non-temporal, as every
+// cache copy of the decode), with no per-copy address
 // arithmetic: the wave's latent row 8w + j of the tile is base + j KiB, read
 // as base (j < 4) or base + 4 KiB (j >= 4) plus an instruction offset of
 // (j & 3) KiB, and it lands at stage + lat_row(8w + j) = stage + lat_row(8w)
@@ -224,12 +225,12 @@ __device__ __forceinline__ void issue_fast(const FastCopy& c, const FastLane& fl
     constexpr int off = (J & 3) * LAT_ROW;
     constexpr uint32_t m0_add = lat_row_j(J) - (uint32_t)off;
     const uint8_t* base = J < 4 ? c.lat : c.lat4;
-    asm volatile("s_add_u32 m0, %0, %1\n\tglobal_load_lds_dwordx4 %2, %3 offset:%4"
+    asm volatile("s_add_u32 m0, %0, %1\n\tglobal_load_lds_dwordx4 %2, %3 offset:%4 nt"
                  :
                  : "s"(c.m0_lat), "i"(m0_add), "v"(fl.lat), "s"(base), "i"(off)
                  : "memory", "m0", "scc");
   } else {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                  :
                  : "s"(c.m0_rope), "v"(fl.rope), "s"(c.rope)
                  : "memory", "m0");

@@ -128,7 +128,7 @@ __device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff,
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2 nt"
                :
                : "s"(m0), "v"(voff), "s"((const void*)(uintptr_t)bu)
                : "memory", "m0");

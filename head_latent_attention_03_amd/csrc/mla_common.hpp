@@ -326,6 +326,10 @@ __device__ inline u16x4 lds_read_tr16(const MLA_LDS uint8_t* p) {
 // (lds_base is wave-uniform).  Written as asm so that the compiler's memory
 // model does not see it: otherwise any LDS read it cannot prove disjoint from
 // the copy's destination gets a wait for every outstanding VMEM operation.
+// The copy is non-temporal (nt): the decode reads each cache byte once per
+// launch, and a hint that the stream need not stay in L2 and the last-level
+// cache leaves room there for the weights and partials that the absorb and
+// combine of the same step re-read.
 // The copy has no register result; callers wait for it explicitly with
 // s_waitcnt vmcnt before a barrier, and no compiler-visible VMEM load of the
 // same wave may rely on a vmcnt count made while a copy is outstanding other
@@ -339,7 +343,7 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff,
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
   const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 nt"
                :
                : "s"(m0), "v"(voff), "s"((const void*)(uintptr_t)bu)
                : "memory", "m0");
