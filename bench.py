@@ -696,7 +696,7 @@ def projection_object(launches, tokens=4096, d_model=7168, d_cq=1536, d_c=512, d
     del h, w, out
     torch.cuda.empty_cache()
     return {
-        "kernel": "mla_gemm_bf16 (gemm_nt_kernel)",
+        "kernel": "mla_gemm_bf16 (gemm_nt_wide_kernel, 256 x 160 tiles)",
         "workload": f"latent-down-projection-t{tokens}-dmodel{d_model}-n{n}",
         "bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_PEAK_TFLOPS["bf16"],
         "unit": "TFLOP/s", "frac": round(tfs / MFMA_PEAK_TFLOPS["bf16"], 4),

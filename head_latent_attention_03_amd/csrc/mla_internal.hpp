@@ -103,6 +103,8 @@ struct GemmArgs {            // C[b] = A[b] B[b]^T, bf16 in, fp32 accumulate
   int32_t batch, m, n, k, c_f32;
 };
 hipError_t launch_gemm_nt(const GemmArgs& g, hipStream_t s);
+// which tile launch_gemm_nt takes (true: 256 x 160, false: 128 x 128)
+bool gemm_nt_takes_wide_tiles(const GemmArgs& g);
 
 struct TransposeArgs {       // dst[b][c][r] = src[b][r][c], 16-bit elements
   const void* src;

@@ -28,11 +28,14 @@ def _rel(got, ref):
 
 
 @pytest.mark.parametrize("m,n,k,batch", [(1, 1, 8, 1), (77, 130, 200, 1), (256, 384, 512, 3),
-                                         (300, 129, 1032, 2)])
+                                         (300, 129, 1032, 2), (1300, 2112, 1032, 2),
+                                         (1030, 2000, 520, 3)])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_gemm_matches_oracle(m, n, k, batch, out):
     """Ragged sizes (m, n past a 128 tile, k past a 64 chunk), batched operands with
-    the first one shared by every batch entry; bf16 and f32 outputs."""
+    the first one shared by every batch entry; bf16 and f32 outputs.  The last two
+    shapes (at least 512 rows and 128 tiles of 256 x 160) take the wide-tile kernel,
+    with m past a 256 tile and n past a 160 tile."""
     rng = np.random.default_rng(m * 7 + n + k)
     a, a64 = _bf16(rng, (m, k), 1 / np.sqrt(k))
     b, b64 = _bf16(rng, (batch, n, k))
@@ -45,6 +48,19 @@ def test_gemm_matches_oracle(m, n, k, batch, out):
         ref = oracle.down_project(a64, b64[i])
         r = _rel(got[i], ref)
         assert r <= (1e-5 if out == "f32" else 2e-2), (i, r)
+
+
+def test_gemm_at_the_down_projection_shape():
+    """The 4096-token x 7168 -> 2112 latent down-projection that the projection
+    bench times (wide-tile kernel), every output against the fp64 product."""
+    rng = np.random.default_rng(4096)
+    a, a64 = _bf16(rng, (4096, 7168), 0.02)
+    b, b64 = _bf16(rng, (1, 2112, 7168), 1 / np.sqrt(7168))
+    c = torch.empty((1, 4096, 2112), dtype=torch.bfloat16, device=DEV)
+    B.mla_gemm_bf16(a, b, c)
+    torch.cuda.synchronize()
+    r = _rel(to_f64(c)[0], oracle.down_project(a64, b64[0]))
+    assert r <= 2e-2, r
 
 
 def _dims(H, **kw):
